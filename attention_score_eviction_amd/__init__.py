@@ -1,0 +1,15 @@
+"""WAITS prefill KV selection (score -> top-k select -> compact) on AMD MI355X.
+
+The computation runs in ``libwaits.so`` (hand-written HIP kernels for
+gfx950, C ABI in ``include/waits.h``); ``waits`` is its Python binding.
+"""
+from . import waits  # noqa: F401
+from .waits import (  # noqa: F401
+    WaitsError,
+    colsum,
+    compact,
+    lse,
+    score,
+    score_select_compact,
+    select,
+)

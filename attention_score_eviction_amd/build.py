@@ -1,0 +1,57 @@
+"""Compile the WAITS HIP library (libwaits.so) for gfx950, in-tree.
+
+``python -m attention_score_eviction_amd.build`` or ``build_library()``.
+Always recompiles; the library lands next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libwaits.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libwaits.so)")
+
+
+def compile_command(out: str) -> list:
+    return [
+        _hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+        # no packed fp32 VALU instructions in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", INCLUDE, "-I", CSRC,
+        os.path.join(CSRC, "waits_api.hip"), "-o", out,
+    ]
+
+
+def build_library(verbose: bool = False) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = compile_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops" not in ln]  # host pass does not know the feature
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,439 @@
+// Host side of the WAITS C ABI (include/waits.h): argument checks, launch
+// planning and kernel launches on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "waits.h"
+#include "device_common.hpp"
+#include "kernel_args.hpp"
+#include "pass1_lse.hpp"
+#include "pass2_colsum.hpp"
+#include "select_compact.hpp"
+
+namespace waits {
+namespace {
+
+// Tile configuration (stationary 32-row tiles per wave).
+constexpr int SW1 = 2;                            // pass 1: 64 query rows per wave
+constexpr int SW2 = 2;                            // pass 2: 64 keys per wave
+constexpr int WGROWS1 = NWAVES * SW1 * TILE;      // 256 packed rows per workgroup
+constexpr int WGKEYS2 = NWAVES * SW2 * TILE;      // 256 keys per workgroup
+constexpr int NUM_CU = 256;
+constexpr int MAX_SEQ_LEN = (1 << 22) - 1;        // keeps N - b - 0.5 exact in fp32
+constexpr int MAX_B = 1 << 22;
+constexpr float LIVE_EXP_LIMIT = 89.0f;           // expf overflows above ~88.7228
+
+struct Seq {
+  int n = 0, q0 = 0, pr = 0;
+  int rg = 0, nc = 1, kc = 32;
+  int64_t tok0 = 0;
+  float a = 0.f, c = 0.f;
+};
+
+bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elt_bytes(int dtype) { return dtype == WAITS_BF16 ? 2 : 4; }
+
+int check_shape(const waits_shape* s, bool need_q) {
+  if (!s || !s->cu_seqlens || s->batch < 1) return WAITS_EINVAL;
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads) return WAITS_EINVAL;
+  if (s->cu_seqlens[0] != 0) return WAITS_EINVAL;
+  for (int i = 0; i < s->batch; ++i) {
+    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
+  }
+  if (s->dtype != WAITS_BF16 && s->dtype != WAITS_F32) return WAITS_EINVAL;
+  if (s->head_dim < 1) return WAITS_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return WAITS_EUNSUPPORTED;
+  const int64_t e = elt_bytes(s->dtype);
+  if (s->kv_stride_tok < 0 || s->kv_stride_head < 0) return WAITS_EINVAL;
+  if ((s->kv_stride_tok * e) % 16 || (s->kv_stride_head * e) % 16) return WAITS_EINVAL;
+  if (need_q) {
+    if (s->q_stride_tok < 0 || s->q_stride_head < 0) return WAITS_EINVAL;
+    if ((s->q_stride_tok * e) % 16 || (s->q_stride_head * e) % 16) return WAITS_EINVAL;
+    if (!(std::isfinite(s->scale) && s->scale > 0.f)) return WAITS_EINVAL;
+  }
+  return WAITS_OK;
+}
+
+int check_curves(const waits_shape* s, const float* a, const int32_t* b) {
+  if (!a || !b) return WAITS_EINVAL;
+  for (int i = 0; i < s->batch; ++i) {
+    if (std::isnan(a[i]) || a[i] < 0.f) return WAITS_EINVAL;
+    if (b[i] < 1 || b[i] > MAX_B) return WAITS_EINVAL;
+  }
+  return WAITS_OK;
+}
+
+// First row whose fp32 weight can be nonzero.  w = 1 / (1 + expf(a (c - q)))
+// is exactly 0 only where expf overflows, i.e. a (c - q) > 88.72..; rows are
+// kept from the first q with a (c - q) <= 89 (fp32 product, as on the
+// device), so every row left out has an fp32 weight of exactly 0 whatever the
+// last-ulp behaviour of expf.  Row N - 1 always has w >= 1/2.
+int first_live_row(int n, float a, int32_t b) {
+  if (n <= 0) return 0;
+  const float c = (float)n - (float)b - 0.5f;
+  auto dead = [&](int q) { return a * (c - (float)q) > LIVE_EXP_LIMIT; };
+  if (a == 0.f) return 0;
+  int q;
+  if (std::isinf(a)) {
+    q = std::max(0, (int)std::ceil((double)c));
+  } else {
+    const double est = (double)c - (double)LIVE_EXP_LIMIT / (double)a;
+    q = (int)std::max(0.0, std::min((double)n - 1, std::floor(est) - 2.0));
+  }
+  while (q > 0 && !dead(q - 1)) --q;
+  while (q < n - 1 && dead(q)) ++q;
+  return std::min(q, n - 1);
+}
+
+std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b) {
+  const int G = s->n_q_heads / s->n_kv_heads;
+  std::vector<Seq> v(s->batch);
+  for (int i = 0; i < s->batch; ++i) {
+    Seq& q = v[i];
+    q.n = (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]);
+    q.tok0 = s->cu_seqlens[i];
+    q.a = a ? a[i] : 0.f;
+    q.c = (float)q.n - (float)(b ? b[i] : 1) - 0.5f;
+    q.q0 = a ? first_live_row(q.n, a[i], b[i]) : 0;
+    q.pr = G * (q.n - q.q0);
+    q.rg = (q.pr + WGROWS1 - 1) / WGROWS1;
+    q.nc = 1;
+    q.kc = std::max(32, (q.n + 31) / 32 * 32);
+  }
+  // Split the key range when rows alone give too few workgroups.
+  int64_t total_rg = 0;
+  for (const Seq& q : v) total_rg += (int64_t)s->n_kv_heads * q.rg;
+  if (total_rg > 0 && total_rg < 2 * NUM_CU) {
+    const int want = (int)((4 * NUM_CU + total_rg - 1) / total_rg);
+    for (Seq& q : v) {
+      if (q.n == 0) continue;
+      const int nc = std::max(1, std::min(want, (q.n + 511) / 512));
+      q.kc = ((q.n + nc - 1) / nc + 31) / 32 * 32;
+      q.nc = (q.n + q.kc - 1) / q.kc;
+    }
+  }
+  return v;
+}
+
+// Partial (float2) slots pass 1 needs for sequences [lo, hi).
+int64_t partial_slots(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
+  int64_t tot = 0;
+  for (int i = lo; i < hi; ++i)
+    if (v[i].nc > 1) tot += (int64_t)s->n_kv_heads * v[i].rg * WGROWS1 * v[i].nc;
+  return tot;
+}
+
+size_t lse_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+  int64_t mx = 0;
+  for (int lo = 0; lo < s->batch; lo += MAXB)
+    mx = std::max(mx, partial_slots(s, v, lo, std::min(s->batch, lo + MAXB)));
+  return (size_t)mx * sizeof(float2);
+}
+
+size_t lse_buffer_bytes(const waits_shape* s) {
+  const size_t bytes = (size_t)s->n_q_heads * (size_t)s->cu_seqlens[s->batch] * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+void fill_table(SeqTable& t, const std::vector<Seq>& v, int lo, int hi) {
+  std::memset(&t, 0, sizeof(t));
+  t.nb = hi - lo;
+  for (int i = lo; i < hi; ++i) {
+    const Seq& q = v[i];
+    const int j = i - lo;
+    t.n[j] = q.n;
+    t.q0[j] = q.q0;
+    t.rg[j] = q.rg;
+    t.nc[j] = q.nc;
+    t.kc[j] = q.kc;
+    t.a[j] = q.a;
+    t.c[j] = q.c;
+    t.tok0[j] = q.tok0;
+  }
+}
+
+Strides strides_of(const waits_shape* s) {
+  return Strides{s->q_stride_tok, s->q_stride_head, s->kv_stride_tok, s->kv_stride_head};
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? WAITS_OK : WAITS_EDEVICE; }
+
+template <typename T, int D>
+void launch_lse(const LseArgs& args, int items, hipStream_t st) {
+  hipLaunchKernelGGL((lse_kernel<T, D, SW1>), dim3(items), dim3(NTHREADS), 0, st, args);
+}
+
+template <typename T, int D>
+void launch_colsum(const ColsumArgs& args, int items, hipStream_t st) {
+  hipLaunchKernelGGL((colsum_kernel<T, D, SW2>), dim3(items), dim3(NTHREADS), 0, st, args);
+}
+
+int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, const int32_t* b,
+            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const std::vector<Seq> v = plan_seqs(s, a, b);
+  if (ws_bytes < lse_ws_bytes(s, v) || (lse_ws_bytes(s, v) > 0 && !ws)) return WAITS_EWORKSPACE;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    LseArgs args;
+    args.q = q;
+    args.k = k;
+    args.lse = lse;
+    args.part = static_cast<float2*>(ws);
+    args.st = strides_of(s);
+    args.T = s->cu_seqlens[s->batch];
+    args.G = G;
+    args.hkv = s->n_kv_heads;
+    args.scale = s->scale;
+    args.scale_log2 = s->scale * LOG2E;
+    fill_table(args.tab, v, lo, hi);
+    int items = 0;
+    int64_t ws0 = 0;
+    for (int i = lo; i < hi; ++i) {
+      args.tab.first[i - lo] = items;
+      args.tab.ws0[i - lo] = ws0;
+      items += s->n_kv_heads * v[i].rg * v[i].nc;
+      if (v[i].nc > 1) ws0 += (int64_t)s->n_kv_heads * v[i].rg * WGROWS1 * v[i].nc;
+    }
+    args.tab.first[hi - lo] = items;
+    if (items == 0) continue;
+    if (s->dtype == WAITS_BF16) {
+      if (s->head_dim == 64) launch_lse<bf16_t, 64>(args, items, stream);
+      else launch_lse<bf16_t, 128>(args, items, stream);
+    } else {
+      if (s->head_dim == 64) launch_lse<float, 64>(args, items, stream);
+      else launch_lse<float, 128>(args, items, stream);
+    }
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+
+    if (ws0 > 0) {
+      CombineArgs cargs;
+      cargs.lse = lse;
+      cargs.part = static_cast<const float2*>(ws);
+      cargs.T = args.T;
+      cargs.G = G;
+      cargs.hkv = s->n_kv_heads;
+      cargs.wgrows = WGROWS1;
+      cargs.tab = args.tab;
+      int rows = 0;
+      for (int i = lo; i < hi; ++i) {
+        cargs.tab.first[i - lo] = rows;
+        if (v[i].nc > 1) rows += s->n_kv_heads * v[i].pr;
+      }
+      cargs.tab.first[hi - lo] = rows;
+      hipLaunchKernelGGL(lse_combine_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, cargs);
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+  }
+  return WAITS_OK;
+}
+
+int run_colsum(const waits_shape* s, const void* q, const void* k, const float* lse,
+               const float* a, const int32_t* b, float* scores, hipStream_t stream) {
+  const std::vector<Seq> v = plan_seqs(s, a, b);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    ColsumArgs args;
+    args.q = q;
+    args.k = k;
+    args.lse = lse;
+    args.scores = scores;
+    args.st = strides_of(s);
+    args.T = s->cu_seqlens[s->batch];
+    args.G = G;
+    args.hkv = s->n_kv_heads;
+    args.scale_log2 = s->scale * LOG2E;
+    fill_table(args.tab, v, lo, hi);
+    int items = 0;
+    for (int i = lo; i < hi; ++i) {
+      args.tab.first[i - lo] = items;
+      items += s->n_kv_heads * ((v[i].n + WGKEYS2 - 1) / WGKEYS2);
+    }
+    args.tab.first[hi - lo] = items;
+    if (items == 0) continue;
+    if (s->dtype == WAITS_BF16) {
+      if (s->head_dim == 64) launch_colsum<bf16_t, 64>(args, items, stream);
+      else launch_colsum<bf16_t, 128>(args, items, stream);
+    } else {
+      if (s->head_dim == 64) launch_colsum<float, 64>(args, items, stream);
+      else launch_colsum<float, 128>(args, items, stream);
+    }
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
+}  // namespace
+}  // namespace waits
+
+using namespace waits;
+
+extern "C" {
+
+int waits_first_rows(const waits_shape* s, const float* a, const int32_t* b, int32_t* first_row) {
+  if (!s || !s->cu_seqlens || s->batch < 1 || s->cu_seqlens[0] != 0 || !first_row)
+    return WAITS_EINVAL;
+  for (int i = 0; i < s->batch; ++i) {
+    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
+  }
+  const int rc = check_curves(s, a, b);
+  if (rc != WAITS_OK) return rc;
+  for (int i = 0; i < s->batch; ++i)
+    first_row[i] = first_live_row((int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]), a[i], b[i]);
+  return WAITS_OK;
+}
+
+int waits_lse_workspace_bytes(const waits_shape* s, const float* a, const int32_t* b,
+                              size_t* bytes) {
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
+  if (rc != WAITS_OK) return rc;
+  *bytes = lse_ws_bytes(s, plan_seqs(s, a, b));
+  return WAITS_OK;
+}
+
+int waits_score_workspace_bytes(const waits_shape* s, const float* a, const int32_t* b,
+                                size_t* bytes) {
+  size_t part = 0;
+  const int rc = waits_lse_workspace_bytes(s, a, b, &part);
+  if (rc != WAITS_OK) return rc;
+  *bytes = lse_buffer_bytes(s) + part;
+  return WAITS_OK;
+}
+
+int waits_lse(const waits_shape* s, const void* q, const void* k, const float* a,
+              const int32_t* b, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc != WAITS_OK) return rc;
+  if (s->cu_seqlens[s->batch] == 0) return WAITS_OK;
+  if (!q || !k || !lse || !is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(lse, 4))
+    return WAITS_EINVAL;
+  return run_lse(s, q, k, a, b, lse, ws, ws_bytes, stream);
+}
+
+int waits_colsum(const waits_shape* s, const void* q, const void* k, const float* lse,
+                 const float* a, const int32_t* b, float* scores, hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc != WAITS_OK) return rc;
+  if (s->cu_seqlens[s->batch] == 0) return WAITS_OK;
+  if (!q || !k || !lse || !scores || !is_aligned(q, 16) || !is_aligned(k, 16) ||
+      !is_aligned(lse, 4) || !is_aligned(scores, 4))
+    return WAITS_EINVAL;
+  return run_colsum(s, q, k, lse, a, b, scores, stream);
+}
+
+int waits_score(const waits_shape* s, const void* q, const void* k, const float* a,
+                const int32_t* b, float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc != WAITS_OK) return rc;
+  if (s->cu_seqlens[s->batch] == 0) return WAITS_OK;
+  if (!q || !k || !scores || !is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(scores, 4))
+    return WAITS_EINVAL;
+  const std::vector<Seq> v = plan_seqs(s, a, b);
+  const size_t lse_bytes = lse_buffer_bytes(s);
+  const size_t need = lse_bytes + lse_ws_bytes(s, v);
+  if (!ws || ws_bytes < need || !is_aligned(ws, 256)) return WAITS_EWORKSPACE;
+  float* lse = static_cast<float*>(ws);
+  void* part = static_cast<unsigned char*>(ws) + lse_bytes;
+  rc = run_lse(s, q, k, a, b, lse, part, ws_bytes - lse_bytes, stream);
+  if (rc != WAITS_OK) return rc;
+  return run_colsum(s, q, k, lse, a, b, scores, stream);
+}
+
+int waits_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
+                 hipStream_t stream) {
+  if (!s || !s->cu_seqlens || s->batch < 1 || s->n_kv_heads < 1 || s->cu_seqlens[0] != 0)
+    return WAITS_EINVAL;
+  int maxn = 0;
+  for (int i = 0; i < s->batch; ++i) {
+    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
+    maxn = std::max(maxn, (int)n);
+  }
+  if (budget < 1 || !idx || !is_aligned(idx, 4)) return WAITS_EINVAL;
+  if (s->cu_seqlens[s->batch] > 0 && (!scores || !is_aligned(scores, 4))) return WAITS_EINVAL;
+  const std::vector<Seq> v = plan_seqs(s, nullptr, nullptr);
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    SelectArgs args;
+    args.scores = scores;
+    args.idx = idx + (int64_t)lo * s->n_kv_heads * budget;
+    args.T = s->cu_seqlens[s->batch];
+    args.hkv = s->n_kv_heads;
+    args.budget = budget;
+    fill_table(args.tab, v, lo, hi);
+    int gmax = 0;
+    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+    const dim3 grid((hi - lo) * s->n_kv_heads);
+    if (gmax <= SEL_THREADS * 16)
+      hipLaunchKernelGGL(select_kernel<16>, grid, dim3(SEL_THREADS), 0, stream, args);
+    else if (gmax <= SEL_THREADS * 32)
+      hipLaunchKernelGGL(select_kernel<32>, grid, dim3(SEL_THREADS), 0, stream, args);
+    else
+      hipLaunchKernelGGL(select_kernel<0>, grid, dim3(SEL_THREADS), 0, stream, args);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  (void)maxn;
+  return WAITS_OK;
+}
+
+int waits_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
+                  int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
+  const int rc = check_shape(s, false);
+  if (rc != WAITS_OK) return rc;
+  if (budget < 1 || !idx || !k_out || !v_out || !is_aligned(idx, 4) || !is_aligned(k_out, 16) ||
+      !is_aligned(v_out, 16))
+    return WAITS_EINVAL;
+  if (s->cu_seqlens[s->batch] > 0 && (!k || !v || !is_aligned(k, 16) || !is_aligned(v, 16)))
+    return WAITS_EINVAL;
+  const std::vector<Seq> sq = plan_seqs(s, nullptr, nullptr);
+  const int e = elt_bytes(s->dtype);
+  const int row_bytes = s->head_dim * e;
+  const int rows_per_block = 256 / (row_bytes / 16);
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
+    CompactArgs args;
+    args.k = static_cast<const unsigned char*>(k);
+    args.v = static_cast<const unsigned char*>(v);
+    args.idx = idx + first_row;
+    args.k_out = static_cast<unsigned char*>(k_out) + first_row * row_bytes;
+    args.v_out = static_cast<unsigned char*>(v_out) + first_row * row_bytes;
+    args.st = strides_of(s);
+    args.rows = (int64_t)(hi - lo) * s->n_kv_heads * budget;
+    args.hkv = s->n_kv_heads;
+    args.budget = budget;
+    args.elt = e;
+    fill_table(args.tab, sq, lo, hi);
+    const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
+const char* waits_strerror(int code) {
+  switch (code) {
+    case WAITS_OK: return "ok";
+    case WAITS_EINVAL: return "invalid argument";
+    case WAITS_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128)";
+    case WAITS_EWORKSPACE: return "workspace missing or too small";
+    case WAITS_EDEVICE: return "HIP runtime refused a kernel launch";
+    default: return "unknown WAITS status";
+  }
+}
+
+}  // extern "C"

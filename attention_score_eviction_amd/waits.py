@@ -1,0 +1,294 @@
+"""Python binding of libwaits.so (include/waits.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module turns torch
+tensors into pointers, strides and the caller's current HIP stream, and
+raises ``WaitsError`` on a nonzero status.  There is no fallback: if the
+library is not built, every call raises.
+
+Layouts (token-major packed batch, positions restart per sequence):
+  q [T, Hq, d], k / v [T, Hkv, d]  (any strides with d contiguous)
+  lse [Hq, T] fp32, scores [Hkv, T] fp32
+  idx [B, Hkv, budget] int32, k_out / v_out [B, Hkv, budget, d]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional, Sequence, Union
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwaits.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "waits.h")
+
+WAITS_OK, WAITS_EINVAL, WAITS_EUNSUPPORTED, WAITS_EWORKSPACE, WAITS_EDEVICE = range(5)
+WAITS_BF16, WAITS_F32 = 0, 1
+
+
+class WaitsError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {strerror(code)} (status {code})")
+        self.code = code
+
+
+class WaitsShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("q_stride_tok", ctypes.c_int64),
+        ("q_stride_head", ctypes.c_int64),
+        ("kv_stride_tok", ctypes.c_int64),
+        ("kv_stride_head", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(WaitsShape)
+_FP = ctypes.POINTER(ctypes.c_float)
+_IP = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "waits_first_rows": [_SP, _FP, _IP, _IP],
+    "waits_lse_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
+    "waits_score_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
+    "waits_lse": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
+    "waits_colsum": [_SP, _P, _P, _P, _FP, _IP, _P, _P],
+    "waits_score": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
+    "waits_select": [_SP, _P, ctypes.c_int32, _P, _P],
+    "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m attention_score_eviction_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        handle.waits_strerror.argtypes = [ctypes.c_int]
+        handle.waits_strerror.restype = ctypes.c_char_p
+        _lib = handle
+    return _lib
+
+
+def header_symbols() -> list:
+    """Entry points declared in include/waits.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(waits_\w+)\s*\(", text, re.M)))
+
+
+def strerror(code: int) -> str:
+    return lib().waits_strerror(int(code)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != WAITS_OK:
+        raise WaitsError(fn, rc)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+class _Marshal:
+    """Host-side argument block for one call (keeps the host arrays alive)."""
+
+    def __init__(self, cu_seqlens, q: Optional[torch.Tensor], kv: torch.Tensor,
+                 scale: Optional[float], a=None, b=None, n_q_heads: Optional[int] = None):
+        self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        batch = len(self.cu) - 1
+        if kv.dtype == torch.bfloat16:
+            dt = WAITS_BF16
+        elif kv.dtype == torch.float32:
+            dt = WAITS_F32
+        else:
+            raise TypeError(f"K/V must be bfloat16 or float32, got {kv.dtype}")
+        if q is not None and q.dtype != kv.dtype:
+            raise TypeError("Q and K must share a dtype")
+        d = kv.shape[-1]
+        self.shape = WaitsShape()
+        self.shape.batch = batch
+        self.shape.cu_seqlens = self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        self.shape.n_kv_heads = kv.shape[1]
+        self.shape.n_q_heads = q.shape[1] if q is not None else (n_q_heads or kv.shape[1])
+        self.shape.head_dim = d
+        self.shape.dtype = dt
+        self.shape.kv_stride_tok, self.shape.kv_stride_head = kv.stride(0), kv.stride(1)
+        if q is not None:
+            self.shape.q_stride_tok, self.shape.q_stride_head = q.stride(0), q.stride(1)
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        self.shape.scale = float(scale)
+        self.a = self.b = None
+        if a is not None:
+            self.a = np.ascontiguousarray(np.broadcast_to(np.asarray(a, np.float32), (batch,)))
+            self.b = np.ascontiguousarray(np.broadcast_to(np.asarray(b, np.int32), (batch,)))
+
+    @property
+    def sp(self):
+        return ctypes.byref(self.shape)
+
+    @property
+    def ap(self):
+        return self.a.ctypes.data_as(_FP)
+
+    @property
+    def bp(self):
+        return self.b.ctypes.data_as(_IP)
+
+
+def _last_dim_contiguous(*ts):
+    for t in ts:
+        if t is not None and t.stride(-1) != 1:
+            raise ValueError("the head_dim axis must be contiguous")
+
+
+def first_rows(cu_seqlens, a, b) -> np.ndarray:
+    """First processed query row of every sequence (host-only query)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    nb = len(cu) - 1
+    shape = WaitsShape()
+    shape.batch = nb
+    shape.cu_seqlens = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    a32 = np.ascontiguousarray(np.broadcast_to(np.asarray(a, np.float32), (nb,)))
+    b32 = np.ascontiguousarray(np.broadcast_to(np.asarray(b, np.int32), (nb,)))
+    out = np.zeros(nb, dtype=np.int32)
+    _check("waits_first_rows", lib().waits_first_rows(
+        ctypes.byref(shape), a32.ctypes.data_as(_FP), b32.ctypes.data_as(_IP),
+        out.ctypes.data_as(_IP)))
+    return out
+
+
+def lse_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    out = ctypes.c_size_t(0)
+    _check("waits_lse_workspace_bytes",
+           lib().waits_lse_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
+    return out.value
+
+
+def score_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    out = ctypes.c_size_t(0)
+    _check("waits_score_workspace_bytes",
+           lib().waits_score_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+def lse(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
+        out: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pass 1: per-row natural-log normaliser, [Hq, T] fp32 (processed rows)."""
+    _last_dim_contiguous(q, k)
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    if out is None:
+        out = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    nbytes = lse_workspace_bytes(q, k, cu_seqlens, a, b, scale)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check("waits_lse", lib().waits_lse(
+        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), _ptr(ws),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
+    return out
+
+
+def colsum(q: torch.Tensor, k: torch.Tensor, lse_rows: torch.Tensor, cu_seqlens, a, b,
+           scale=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pass 2: WAITS key scores [Hkv, T] fp32 from the pass-1 normalisers."""
+    _last_dim_contiguous(q, k)
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    if out is None:
+        out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
+    _check("waits_colsum", lib().waits_colsum(
+        m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), _stream(q)))
+    return out
+
+
+def score(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
+          out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Both passes: WAITS key scores [Hkv, T] fp32."""
+    _last_dim_contiguous(q, k)
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    if out is None:
+        out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
+    nbytes = score_workspace_bytes(q, k, cu_seqlens, a, b, scale)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check("waits_score", lib().waits_score(
+        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), _ptr(ws),
+        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
+    return out
+
+
+def select(scores: torch.Tensor, cu_seqlens, budget: int,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-``budget`` key positions per (sequence, KV head), ascending, -1 padded."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    hkv = scores.shape[0]
+    if out is None:
+        out = torch.empty((len(cu) - 1, hkv, int(budget)), dtype=torch.int32,
+                          device=scores.device)
+    shape = WaitsShape()
+    cu_c = np.ascontiguousarray(cu)
+    shape.batch = len(cu_c) - 1
+    shape.cu_seqlens = cu_c.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    shape.n_kv_heads = hkv
+    shape.n_q_heads = hkv
+    _check("waits_select", lib().waits_select(
+        ctypes.byref(shape), _ptr(scores), int(budget), _ptr(out), _stream(scores)))
+    return out
+
+
+def compact(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, cu_seqlens, budget: int,
+            k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None):
+    """Gather the selected K/V rows into [B, Hkv, budget, d] (bit-exact)."""
+    _last_dim_contiguous(k, v)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    m = _Marshal(cu_seqlens, None, k, 1.0)
+    nb, hkv, d = len(m.cu) - 1, k.shape[1], k.shape[2]
+    if k_out is None:
+        k_out = torch.empty((nb, hkv, int(budget), d), dtype=k.dtype, device=k.device)
+    if v_out is None:
+        v_out = torch.empty((nb, hkv, int(budget), d), dtype=v.dtype, device=v.device)
+    _check("waits_compact", lib().waits_compact(
+        m.sp, _ptr(k), _ptr(v), _ptr(idx), int(budget), _ptr(k_out), _ptr(v_out), _stream(k)))
+    return k_out, v_out
+
+
+def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None):
+    """The whole path: scores, kept positions and the compacted K/V."""
+    s = score(q, k, cu_seqlens, a, b, scale)
+    idx = select(s, cu_seqlens, budget)
+    kc, vc = compact(k, v, idx, cu_seqlens, budget)
+    return s, idx, kc, vc

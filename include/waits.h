@@ -1,0 +1,166 @@
+/*
+ * waits.h -- C ABI of the WAITS prefill KV-selection path on AMD MI355X
+ * (gfx950): score every prompt key, keep the top keys per KV head, gather
+ * the kept K/V rows into a compacted cache.
+ *
+ * Method (WAITS README, page "Dirac-Notation/A2SF", introduction): a prompt
+ * key's score is the causal softmax attention it receives, summed over all
+ * query rows of the prompt with the sigmoid forgetting-curve weight
+ *     w[q] = 1 / (1 + exp(-a (q - (N - b - 0.5)))),   q = 0 .. N-1,
+ * and the cache keeps the highest-scoring keys.  a = 0 is H2O, a = +inf with
+ * b = 1 is TOVA, a = +inf with b = window is SnapKV.  The README's
+ * "Quickstart" names the knobs: sigmoid_a (a), recent_budget (b) and
+ * select_budget (keys kept per KV head); "Repository layout" names the top-k
+ * selector.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - A batch is `batch` independent sequences (prompts, or layers of one
+ *   prompt) packed along a token axis of T = cu_seqlens[batch] tokens.
+ *   Positions q, k restart at 0 in every sequence.
+ * - Q is [T, n_q_heads, head_dim], K and V are [T, n_kv_heads, head_dim],
+ *   addressed with element strides (q_stride_tok, q_stride_head) and
+ *   (kv_stride_tok, kv_stride_head); the head_dim axis is contiguous.  K and
+ *   V share strides.  Every row must start on a 16-byte boundary.
+ * - Query head g reads KV head g / G, G = n_q_heads / n_kv_heads; a KV
+ *   head's score sums its G query heads.
+ * - dtype WAITS_BF16: bf16 inputs, bf16 x bf16 products accumulated in
+ *   fp32; WAITS_F32: fp32 inputs and fp32 arithmetic.  Softmax, weights and
+ *   scores are fp32.
+ * - Ownership: the caller allocates every buffer (device memory unless the
+ *   argument says host).  The library allocates nothing, frees nothing,
+ *   keeps no state between calls and never synchronises: it enqueues
+ *   kernels on `stream` and returns.  Results are ready when the stream is.
+ * - Errors: every argument is checked on the host before anything is
+ *   enqueued; a failed check returns a nonzero WAITS_E* code and enqueues
+ *   nothing.  WAITS_EDEVICE reports a launch the HIP runtime refused; faults
+ *   inside kernels surface at the caller's next synchronisation.
+ * - Per-sequence limits: 0 <= N < 2^23 (so N - b - 0.5 is exact in fp32).
+ */
+#ifndef WAITS_H
+#define WAITS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  WAITS_OK = 0,
+  WAITS_EINVAL = 1,       /* malformed argument (null, negative, NaN, ...) */
+  WAITS_EUNSUPPORTED = 2, /* well-formed but not built (head_dim, dtype)   */
+  WAITS_EWORKSPACE = 3,   /* workspace missing or smaller than required    */
+  WAITS_EDEVICE = 4       /* the HIP runtime refused a launch              */
+};
+
+enum { WAITS_BF16 = 0, WAITS_F32 = 1 };
+
+typedef struct waits_shape {
+  int32_t batch;              /* number of sequences, >= 1                     */
+  const int64_t* cu_seqlens;  /* HOST array [batch + 1], cu[0] = 0, ascending */
+  int32_t n_q_heads;          /* >= 1, multiple of n_kv_heads                  */
+  int32_t n_kv_heads;         /* >= 1                                          */
+  int32_t head_dim;           /* 64 or 128                                     */
+  int32_t dtype;              /* WAITS_BF16 or WAITS_F32                       */
+  int64_t q_stride_tok, q_stride_head;   /* element strides of Q          */
+  int64_t kv_stride_tok, kv_stride_head; /* element strides of K and V    */
+  float scale;                /* softmax scale, finite > 0 (1/sqrt(head_dim)) */
+} waits_shape;
+
+/*
+ * a[i], b[i] (HOST arrays [batch]): the forgetting curve of sequence i.
+ * a in [0, +inf] (NaN and negative values are rejected); b >= 1 (b > N is
+ * allowed and weights every row).  a = +inf is evaluated with IEEE
+ * arithmetic: N - b - 0.5 is a half-integer, so w is exactly 0 or 1.
+ *
+ * Only query rows whose fp32 weight is nonzero can change a score; the
+ * library processes every row from the first one whose fp32 weight can be
+ * nonzero to the end of the sequence and skips the rows before it, whose
+ * fp32 weight is exactly 0.
+ */
+
+/*
+ * Host-only planning query (enqueues nothing, touches no device): for every
+ * sequence i, first_row[i] receives the first query row the library
+ * processes.  Every row q < first_row[i] has fp32 a * (c - q) > 89 with
+ * c = N - b - 0.5, so expf overflows and its fp32 weight is exactly 0.
+ * first_row: HOST int32 [batch].
+ */
+int waits_first_rows(const waits_shape* shape, const float* a, const int32_t* b,
+                     int32_t* first_row);
+
+/* Bytes of device workspace waits_lse needs for this batch (0 is possible). */
+int waits_lse_workspace_bytes(const waits_shape* shape, const float* a,
+                              const int32_t* b, size_t* bytes);
+
+/*
+ * Pass 1, per-row log-sum-exp (README introduction: the softmax normaliser
+ * of each weighted query row):
+ *   lse[g * T + t] = ln sum_{k <= q} exp(scale * <Q[t, g], K[t0 + k, g / G]>)
+ * for every processed row q (t = t0 + q, t0 = cu_seqlens[i]).
+ * lse: device fp32 [n_q_heads, T], written only at processed rows; other
+ * entries are left untouched.  workspace: device, >= waits_lse_workspace_bytes.
+ */
+int waits_lse(const waits_shape* shape, const void* q, const void* k,
+              const float* a, const int32_t* b, float* lse, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Pass 2, weighted column sums (README introduction: accumulative attention
+ * score under the forgetting curve):
+ *   scores[h * T + t0 + k] = sum_{g in group h} sum_{q >= k}
+ *                            w[q] * exp(scale <Q[t0+q, g], K[t0+k, h]> - lse[g*T+t0+q])
+ * for every key k of every sequence.  lse: as written by waits_lse.
+ * scores: device fp32 [n_kv_heads, T], fully written.
+ */
+int waits_colsum(const waits_shape* shape, const void* q, const void* k,
+                 const float* lse, const float* a, const int32_t* b,
+                 float* scores, hipStream_t stream);
+
+/* Bytes of device workspace waits_score needs (lse buffer + pass-1 workspace). */
+int waits_score_workspace_bytes(const waits_shape* shape, const float* a,
+                                const int32_t* b, size_t* bytes);
+
+/* waits_lse followed by waits_colsum, with lse kept in the workspace. */
+int waits_score(const waits_shape* shape, const void* q, const void* k,
+                const float* a, const int32_t* b, float* scores,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Top-k selection (README "Repository layout": top-k selector): for every
+ * sequence i and KV head h, the min(N_i, select_budget) keys with the
+ * largest score, ties to the lower position, written in ascending position
+ * order to idx[(i * n_kv_heads + h) * select_budget + j] (device int32,
+ * sequence-relative positions); slots j >= N_i hold -1.
+ * scores: device fp32 [n_kv_heads, T], every value >= +0 (as waits_score
+ * writes them).  select_budget >= 1.  Only shape->batch, cu_seqlens and
+ * n_kv_heads are read from `shape`.
+ */
+int waits_select(const waits_shape* shape, const float* scores,
+                 int32_t select_budget, int32_t* idx, hipStream_t stream);
+
+/*
+ * Compaction (README introduction: the retained key-value pairs): copies
+ * the selected rows bit for bit,
+ *   k_out[((i * n_kv_heads + h) * select_budget + j) * head_dim + e]
+ *     = K[cu_seqlens[i] + idx[(i * n_kv_heads + h) * select_budget + j], h, e]
+ * and the same for V; slots whose idx is -1 are zero-filled.  k_out, v_out:
+ * device, dtype of K/V, dense [batch, n_kv_heads, select_budget, head_dim].
+ * idx entries must be -1 or in [0, N_i) (as waits_select writes them).
+ */
+int waits_compact(const waits_shape* shape, const void* k, const void* v,
+                  const int32_t* idx, int32_t select_budget, void* k_out,
+                  void* v_out, hipStream_t stream);
+
+/* Static description of a WAITS_E* code. */
+const char* waits_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAITS_H */

@@ -59,15 +59,24 @@ def _row_softmax(qg: np.ndarray, kh: np.ndarray, rows: np.ndarray,
 
 
 def head_scores(qg: np.ndarray, kh: np.ndarray, w: np.ndarray, scale: float,
-                row_block: int = 256) -> np.ndarray:
+                row_block: int = 256, weight_floor: float = 0.0,
+                row_min: int = 0) -> np.ndarray:
     """Accumulated weighted attention of one KV head.
 
     ``qg[G, N, d]`` are the query heads of the group, ``kh[N, d]`` the keys.
     Returns ``s[k] = sum_g sum_q w[q] A_g[q, k]`` in float64.
+
+    The defaults compute the definition exactly.  For sampled checks at full
+    size two restrictions are available, each with a stated effect:
+    ``weight_floor`` drops rows with ``w[q] <= weight_floor``; since
+    ``A[q, k] <= 1`` the dropped part of any ``s[k]`` is at most
+    ``G * N * weight_floor``.  ``row_min`` drops rows ``q < row_min``; rows
+    only reach keys ``k <= q``, so ``s[k]`` stays exact for ``k >= row_min``.
     """
     n = kh.shape[0]
     s = np.zeros(n, dtype=np.float64)
     rows_all = live_rows(w)
+    rows_all = rows_all[(w[rows_all] > weight_floor) & (rows_all >= row_min)]
     kh = np.asarray(kh, dtype=np.float64)
     for g in range(qg.shape[0]):
         qf = np.asarray(qg[g], dtype=np.float64)
@@ -88,11 +97,13 @@ def _check_packed(q, k, cu_seqlens, n_q_heads, n_kv_heads):
 
 
 def waits_scores(q, k, cu_seqlens, n_q_heads, n_kv_heads, a, b, scale,
-                 row_block: int = 256) -> np.ndarray:
+                 row_block: int = 256, weight_floor: float = 0.0,
+                 row_min=None) -> np.ndarray:
     """Scores ``[Hkv, T]`` for a packed batch.
 
     ``q[T, Hq, d]``, ``k[T, Hkv, d]`` token-major; ``a[i]``, ``b[i]`` per
-    prompt; positions restart at 0 in every prompt.
+    prompt; positions restart at 0 in every prompt.  ``weight_floor`` and
+    ``row_min`` (one value per prompt) restrict rows as in ``head_scores``.
     """
     _check_packed(q, k, cu_seqlens, n_q_heads, n_kv_heads)
     group = n_q_heads // n_kv_heads
@@ -105,7 +116,9 @@ def waits_scores(q, k, cu_seqlens, n_q_heads, n_kv_heads, a, b, scale,
         w = sigmoid_weights(hi - lo, a[p], b[p])
         for h in range(n_kv_heads):
             qg = np.stack([q[lo:hi, h * group + j] for j in range(group)])
-            out[h, lo:hi] = head_scores(qg, k[lo:hi, h], w, scale64, row_block)
+            out[h, lo:hi] = head_scores(
+                qg, k[lo:hi, h], w, scale64, row_block, weight_floor,
+                0 if row_min is None else int(row_min[p]))
     return out
 
 

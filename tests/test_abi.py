@@ -1,0 +1,169 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/waits.h declares, and rejects bad arguments on the host
+before enqueuing anything (no call here reaches a kernel launch)."""
+import ctypes
+import math
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from attention_score_eviction_amd import waits as W
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation
+
+
+def _shape(batch=1, n=64, hq=4, hkv=2, d=64, dtype=W.WAITS_BF16, scale=0.125, cu=None):
+    cu = np.ascontiguousarray(np.asarray(cu if cu is not None else [0, n], np.int64))
+    s = W.WaitsShape()
+    s.batch = batch if cu is None else len(cu) - 1
+    s.cu_seqlens = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    s.n_q_heads, s.n_kv_heads, s.head_dim, s.dtype = hq, hkv, d, dtype
+    s.q_stride_tok, s.q_stride_head = hq * d, d
+    s.kv_stride_tok, s.kv_stride_head = hkv * d, d
+    s.scale = scale
+    s._keep = cu
+    return s
+
+
+def _ab(a=1.0, b=16, n=1):
+    return (np.full(n, a, np.float32), np.full(n, b, np.int32))
+
+
+def _score(shape, a, b, ws_bytes=1 << 30, ws=FAKE):
+    return W.lib().waits_score(ctypes.byref(shape), FAKE, FAKE, a.ctypes.data_as(W._FP),
+                               b.ctypes.data_as(W._IP), FAKE, ws, ws_bytes, None)
+
+
+def test_library_exports_every_declared_symbol():
+    declared = W.header_symbols()
+    assert len(declared) >= 9
+    out = subprocess.run(["nm", "-D", "--defined-only", W.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(W.lib(), name) is not None
+
+
+def test_strerror_codes():
+    assert W.strerror(0) == "ok"
+    for code in (1, 2, 3, 4):
+        assert W.strerror(code) and W.strerror(code) != "ok"
+    assert "unknown" in W.strerror(99)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_q_heads", 3, W.WAITS_EINVAL),        # not a multiple of n_kv_heads
+    ("n_kv_heads", 0, W.WAITS_EINVAL),
+    ("head_dim", 96, W.WAITS_EUNSUPPORTED),
+    ("head_dim", 0, W.WAITS_EINVAL),
+    ("dtype", 7, W.WAITS_EINVAL),
+    ("scale", float("nan"), W.WAITS_EINVAL),
+    ("scale", 0.0, W.WAITS_EINVAL),
+    ("scale", float("inf"), W.WAITS_EINVAL),
+    ("q_stride_tok", 3, W.WAITS_EINVAL),      # row start not 16-byte aligned
+    ("kv_stride_head", -64, W.WAITS_EINVAL),
+])
+def test_shape_validation(field, value, code):
+    s = _shape()
+    setattr(s, field, value)
+    a, b = _ab()
+    assert _score(s, a, b) == code
+
+
+@pytest.mark.parametrize("a,b", [(float("nan"), 16), (-1.0, 16), (1.0, 0), (1.0, -3),
+                                 (1.0, (1 << 22) + 1)])
+def test_curve_validation(a, b):
+    s = _shape()
+    aa, bb = np.array([a], np.float32), np.array([b], np.int32)
+    assert _score(s, aa, bb) == W.WAITS_EINVAL
+    out = ctypes.c_size_t(0)
+    assert W.lib().waits_score_workspace_bytes(ctypes.byref(s), aa.ctypes.data_as(W._FP),
+                                               bb.ctypes.data_as(W._IP),
+                                               ctypes.byref(out)) == W.WAITS_EINVAL
+
+
+def test_cu_seqlens_validation():
+    a, b = _ab(n=2)
+    assert _score(_shape(cu=[1, 5, 9]), a, b) == W.WAITS_EINVAL      # must start at 0
+    assert _score(_shape(cu=[0, 9, 5]), a, b) == W.WAITS_EINVAL      # descending
+    assert _score(_shape(cu=[0, 1 << 22, (1 << 22) + 1]), a, b) == W.WAITS_EINVAL  # too long
+
+
+def test_null_pointers_and_workspace():
+    s = _shape()
+    a, b = _ab()
+    assert W.lib().waits_score(ctypes.byref(s), None, FAKE, a.ctypes.data_as(W._FP),
+                               b.ctypes.data_as(W._IP), FAKE, FAKE, 1 << 30, None) == W.WAITS_EINVAL
+    assert W.lib().waits_score(None, FAKE, FAKE, a.ctypes.data_as(W._FP),
+                               b.ctypes.data_as(W._IP), FAKE, FAKE, 1 << 30, None) == W.WAITS_EINVAL
+    need = ctypes.c_size_t(0)
+    assert W.lib().waits_score_workspace_bytes(ctypes.byref(s), a.ctypes.data_as(W._FP),
+                                               b.ctypes.data_as(W._IP), ctypes.byref(need)) == 0
+    assert need.value >= 4 * 64 * 4
+    assert _score(s, a, b, ws_bytes=need.value - 1) == W.WAITS_EWORKSPACE
+    assert _score(s, a, b, ws=None) == W.WAITS_EWORKSPACE
+    assert _score(s, a, b, ws=ctypes.c_void_p(0x100010)) == W.WAITS_EWORKSPACE  # not 256-aligned
+    assert W.lib().waits_score(ctypes.byref(s), ctypes.c_void_p(0x100002), FAKE,
+                               a.ctypes.data_as(W._FP), b.ctypes.data_as(W._IP), FAKE, FAKE,
+                               1 << 30, None) == W.WAITS_EINVAL   # misaligned Q
+
+
+def test_select_and_compact_validation():
+    s = _shape()
+    lib = W.lib()
+    assert lib.waits_select(ctypes.byref(s), FAKE, 0, FAKE, None) == W.WAITS_EINVAL
+    assert lib.waits_select(ctypes.byref(s), FAKE, 128, None, None) == W.WAITS_EINVAL
+    assert lib.waits_select(ctypes.byref(_shape(cu=[0, -1])), FAKE, 8, FAKE, None) == W.WAITS_EINVAL
+    assert lib.waits_compact(ctypes.byref(s), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == W.WAITS_EINVAL
+    assert lib.waits_compact(ctypes.byref(s), FAKE, FAKE, FAKE, 8, None, FAKE, None) == W.WAITS_EINVAL
+    bad = _shape(d=80)
+    assert lib.waits_compact(ctypes.byref(bad), FAKE, FAKE, FAKE, 8, FAKE, FAKE,
+                             None) == W.WAITS_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("n,a,b", [(4096, 1.0, 16), (16384, 1.0, 16), (16384, 10.0, 1),
+                                   (16384, 10.0, 16), (4096, 0.01, 128), (32768, 0.01, 128),
+                                   (131072, 1.0, 128), (100, 3.5, 200), (1, 10.0, 1),
+                                   (513, 0.0, 1), (2000, math.inf, 16), (2000, math.inf, 5000)])
+def test_first_rows_skip_only_zero_weight_rows(n, a, b):
+    q0 = int(W.first_rows([0, n], [a], [b])[0])
+    a32 = np.float32(a)
+    c = np.float32(n) - np.float32(b) - np.float32(0.5)
+    with np.errstate(over="ignore", invalid="ignore"):
+        x = a32 * (c - np.arange(n, dtype=np.float32))      # fp32, as on the device
+        w = np.float32(1) / (np.float32(1) + np.exp(x))      # fp32 weight
+    # every skipped row overflows expf (ln FLT_MAX = 88.7228...) -> weight exactly 0
+    assert np.all(x[:q0] > np.float32(88.7229))
+    assert np.all(w[:q0] == 0)
+    # and the range is tight: the first processed row is within the 89 margin
+    assert q0 == 0 or x[q0] <= np.float32(89.0)
+    assert q0 <= n - 1
+
+
+def test_first_rows_match_survey_live_counts():
+    # fp32 live-row counts for N = 16384 at the README's five actions
+    n = 16384
+    got = {ab: n - int(W.first_rows([0, n], [ab[0]], [ab[1]])[0])
+           for ab in [(0.0, 1), (1.0, 16), (10.0, 1), (10.0, 16), (math.inf, 16)]}
+    assert got == {(0.0, 1): n, (1.0, 16): 105, (10.0, 1): 10, (10.0, 16): 25,
+                   (math.inf, 16): 16}
+
+
+def test_workspace_sizes():
+    q = torch.empty((4096, 32, 64), dtype=torch.bfloat16)
+    k = torch.empty((4096, 8, 64), dtype=torch.bfloat16)
+    # all rows live: plenty of row groups, no key split, no partials
+    assert W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1]) == 0
+    # 105 live rows: key range split into chunks with (max, sum) partials
+    assert W.lse_workspace_bytes(q, k, [0, 4096], [1.0], [16]) > 0
+    assert W.score_workspace_bytes(q, k, [0, 4096], [0.0], [1]) >= 32 * 4096 * 4
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(W, "_lib", None)
+    monkeypatch.setattr(W, "LIB_PATH", W.LIB_PATH + ".missing")
+    with pytest.raises(RuntimeError, match="missing"):
+        W.lib()

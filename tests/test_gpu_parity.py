@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Sizes: the oracle runs the full definition where it finishes in seconds
+(several tiles plus ragged tails); at the workloads' full sizes it checks
+sampled outputs it can compute exactly (tail keys, or rows above a weight
+floor with a stated bound) plus properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_score_eviction_amd as W
+from oracle import waits_oracle as orc
+from synth import ACTIONS, make_batch, make_prompt
+
+from parity import (DEV, check_compact, check_scores, check_select_exact,
+                    check_select_vs_oracle, host_bits, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _run_all(bt, a, b, budget, scale=None):
+    q, k, v = to_device(bt)
+    cu = bt.cu_seqlens
+    s, idx, kc, vc = W.score_select_compact(q, k, v, cu, a, b, budget, scale)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), idx.cpu().numpy(), kc, vc
+
+
+def _full_check(bt, a, b, budget, scale=None, weight_floor=0.0):
+    d = bt.head_dim
+    scale = np.float32(1 / math.sqrt(d)) if scale is None else np.float32(scale)
+    s_gpu, idx, kc, vc = _run_all(bt, a, b, budget, float(scale))
+    s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, bt.n_q_heads, bt.n_kv_heads,
+                             a, b, float(scale), weight_floor=weight_floor)
+    err = check_scores(s_gpu, s_ref)
+    check_select_exact(idx, s_gpu, bt.cu_seqlens, budget)
+    check_select_vs_oracle(idx, s_ref, bt.cu_seqlens, budget)
+    src_k = bt.k_bits if bt.dtype == "bf16" else bt.k
+    src_v = bt.v_bits if bt.dtype == "bf16" else bt.v
+    check_compact(kc, vc, src_k, src_v, idx, bt.cu_seqlens)
+    return err
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    W.waits.lib()
+    yield
+
+
+# ------------------------------------------------------- the five configs ---
+
+@pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1), (0.0, 16), (math.inf, 1), (math.inf, 16)])
+def test_tiny_fp32(a, b):
+    # 1 layer, 1 query head, 1 KV head, d=64, N=512, fp32 N(0,1), budget 128
+    _say(f"tiny fp32 a={a} b={b}")
+    bt = make_prompt(0, 512, 1, 1, 64, heavy=False, dtype="f32")
+    _full_check(bt, [a], [b], 128)
+
+
+@pytest.fixture(scope="module")
+def llama1b():
+    return make_prompt(1, 4096, 32, 8, 64, heavy=True, dtype="bf16")
+
+
+@pytest.mark.parametrize("a,b", list(ACTIONS))
+def test_llama32_1b_layer(llama1b, a, b):
+    # 32 query heads, 8 KV heads, d=64, N=4096, heavy hitters, budget 128
+    _say(f"llama3.2-1b a={a} b={b}")
+    _full_check(llama1b, [a], [b], 128)
+
+
+def test_llama31_8b_layer_full_size():
+    # one layer of the 8B shape at full size: 32/8/128, N=16384, a=1, b=16
+    _say("llama3.1-8b layer N=16384")
+    bt = make_prompt(1000, 16384, 32, 8, 128, heavy=True, dtype="bf16")
+    # rows with w <= 1e-30 are left out of the oracle: |error| <= G*N*1e-30
+    _full_check(bt, [1.0], [16], 128, weight_floor=1e-30)
+
+
+def test_llama31_8b_layers_batched():
+    # layers are independent sequences of one launch (reduced N)
+    _say("8b-shape 3 layers N=2048 batched")
+    bt = make_batch([1000, 1001, 1002], [2048, 2048, 2048], 32, 8, 128, heavy=True)
+    _full_check(bt, [1.0] * 3, [16] * 3, 128)
+
+
+@pytest.fixture(scope="module")
+def long_prompt():
+    return make_prompt(2, 131072, 32, 8, 128, heavy=True, dtype="bf16")
+
+
+@pytest.mark.parametrize("a,b", [(math.inf, 16), (1.0, 16), (math.inf, 1)])
+def test_long_context_full_size(long_prompt, a, b):
+    # one layer, N=131072, 32/8/128, budget 2048 (few-row regimes: full oracle)
+    _say(f"long N=131072 a={a} b={b}")
+    _full_check(long_prompt, [a], [b], 2048, weight_floor=1e-30)
+
+
+def test_long_context_h2o_sampled(long_prompt):
+    # a=0 at N=131072: every row is live; the oracle checks the last 48 keys
+    # exactly (they only see the last 48 rows) and the mass invariant holds
+    # for every key
+    _say("long N=131072 a=0 sampled")
+    n = 131072
+    bt = long_prompt
+    s_gpu, idx, kc, vc = _run_all(bt, [0.0], [1], 2048)
+    tail = n - 48
+    s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, 32, 8, [0.0], [1],
+                             float(np.float32(1 / math.sqrt(128))), row_min=[tail])
+    check_scores(s_gpu[:, tail:], s_ref[:, tail:])
+    # sum_k s[h, k] = G * sum_q w[q] = 4 * N / 2
+    np.testing.assert_allclose(s_gpu.astype(np.float64).sum(axis=1), 2.0 * n, rtol=1e-4)
+    check_select_exact(idx, s_gpu, bt.cu_seqlens, 2048)
+    check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, bt.cu_seqlens)
+
+
+def _mistral_batch(lo, hi, seed=3):
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi, endpoint=True, size=8)
+    acts = rng.integers(0, 5, size=8)
+    bt = make_batch([3000 + i for i in range(8)], lengths, 32, 8, 128, heavy=True)
+    a = [ACTIONS[j][0] for j in acts]
+    b = [ACTIONS[j][1] for j in acts]
+    return bt, a, b
+
+
+def test_mistral_ragged_batch_reduced():
+    # 8 prompts, ragged lengths, per-prompt (a, b) from the five actions,
+    # budget 256, one launch; lengths cut to [300, 1500] so the oracle is exact
+    _say("mistral ragged reduced")
+    bt, a, b = _mistral_batch(300, 1500)
+    _full_check(bt, a, b, 256)
+
+
+def test_mistral_ragged_batch_full_size():
+    # lengths in [8192, 32768]; tail keys exact, selection and gather exact
+    _say("mistral ragged full size")
+    bt, a, b = _mistral_batch(8192, 32768)
+    s_gpu, idx, kc, vc = _run_all(bt, a, b, 256)
+    cu = bt.cu_seqlens
+    tails = [int(n) - 32 for n in bt.lengths]
+    s_ref = orc.waits_scores(bt.q, bt.k, cu, 32, 8, a, b,
+                             float(np.float32(1 / math.sqrt(128))), row_min=tails)
+    mask = np.zeros(s_gpu.shape, dtype=bool)
+    for p in range(8):
+        mask[:, int(cu[p]) + tails[p]:int(cu[p + 1])] = True
+    check_scores(s_gpu, s_ref, mask=mask)
+    for p in range(8):
+        w = orc.sigmoid_weights(int(bt.lengths[p]), a[p], b[p])
+        got = s_gpu[:, int(cu[p]):int(cu[p + 1])].astype(np.float64).sum(axis=1)
+        np.testing.assert_allclose(got, 4 * w.sum(), rtol=1e-4)
+    check_select_exact(idx, s_gpu, cu, 256)
+    check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, cu)
+
+
+# ------------------------------------------------------------ edge cases ---
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 63, 65, 129, 257, 300])
+@pytest.mark.parametrize("hq,hkv,d", [(1, 1, 64), (2, 1, 128), (8, 1, 64), (16, 2, 128)])
+def test_ragged_small_sizes(n, hq, hkv, d):
+    _say(f"small n={n} hq={hq} hkv={hkv} d={d}")
+    bt = make_prompt(n * 7 + hq, n, hq, hkv, d, heavy=True, dtype="bf16")
+    for a, b in [(1.0, 16), (0.0, 1), (math.inf, 5), (10.0, 1)]:
+        _full_check(bt, [a], [b], 64)
+
+
+def test_batch_with_empty_and_tiny_sequences():
+    _say("batch with empty sequences")
+    bt = make_batch([5, 6, 7, 8, 9], [0, 1, 700, 0, 45], 8, 2, 64, heavy=True)
+    a, b = [1.0, 0.0, 0.01, 1.0, math.inf], [16, 1, 128, 4, 3]
+    _full_check(bt, a, b, 40)
+
+
+def test_b_larger_than_n_and_budget_at_least_n():
+    _say("b > N, budget >= N")
+    bt = make_prompt(11, 200, 4, 2, 64, heavy=True)
+    _full_check(bt, [0.5], [1000], 256)
+    _full_check(bt, [math.inf], [32768], 200)
+
+
+def test_many_sequences_span_launch_groups():
+    # more sequences than one launch's table holds
+    _say("40 sequences")
+    lens = [int(x) for x in np.random.default_rng(4).integers(1, 200, size=40)]
+    bt = make_batch(list(range(100, 140)), lens, 4, 2, 64, heavy=True)
+    acts = [ACTIONS[i % 5] for i in range(40)]
+    _full_check(bt, [x[0] for x in acts], [x[1] for x in acts], 16)
+
+
+def test_all_tied_scores_keep_lowest_positions():
+    # Q = 0 and a = inf, b = 1: the last row is uniform, every score is 1/N
+    _say("all tied")
+    n = 1000
+    q = torch.zeros((n, 4, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((n, 1, 64), device=DEV).to(torch.bfloat16)
+    s = W.score(q, k, [0, n], [math.inf], [1])
+    sc = s.cpu().numpy()
+    assert np.all(sc == sc[0, 0])
+    np.testing.assert_allclose(sc, 4.0 / n, rtol=1e-5)
+    idx = W.select(s, [0, n], 128).cpu().numpy()
+    assert idx[0, 0].tolist() == list(range(128))
+
+
+def test_uniform_attention_closed_form_on_gpu():
+    # Q = 0 at a = 0: s[k] = (G/2)(H_N - H_k) (harmonic numbers)
+    _say("uniform closed form")
+    n, g = 777, 4
+    q = torch.zeros((n, g, 128), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((n, 1, 128), device=DEV).to(torch.bfloat16)
+    s = W.score(q, k, [0, n], [0.0], [1]).cpu().numpy()[0].astype(np.float64)
+    harm = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(s, g / 2 * (harm[n] - harm[:n]), rtol=2e-5)
+
+
+def test_head_major_strides_match_token_major():
+    _say("head-major strides")
+    bt = make_prompt(21, 999, 8, 2, 128, heavy=True)
+    q, k, v = to_device(bt)
+    qh = q.permute(1, 0, 2).contiguous().permute(1, 0, 2)   # [T, H, d] view of [H, T, d]
+    kh = k.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    assert qh.stride(0) == 128 and kh.stride(1) == 999 * 128
+    s1 = W.score(q, k, bt.cu_seqlens, [1.0], [16])
+    s2 = W.score(qh, kh, bt.cu_seqlens, [1.0], [16])
+    assert torch.equal(s1, s2)
+
+
+def test_deterministic_and_causal_support():
+    # bitwise reproducible; perturbing query rows < k0 leaves scores of keys
+    # >= k0 bitwise unchanged (rows only reach keys at or before them)
+    _say("determinism + causal support")
+    bt = make_prompt(31, 3000, 16, 4, 64, heavy=True)
+    q, k, _ = to_device(bt)
+    s1 = W.score(q, k, bt.cu_seqlens, [0.002], [64])
+    s2 = W.score(q, k, bt.cu_seqlens, [0.002], [64])
+    assert torch.equal(s1, s2)
+    k0 = 1234
+    q2 = q.clone()
+    q2[:k0] = torch.randn_like(q2[:k0], dtype=torch.float32).to(torch.bfloat16)
+    s3 = W.score(q2, k, bt.cu_seqlens, [0.002], [64])
+    assert torch.equal(s1[:, k0:], s3[:, k0:])
+    assert not torch.equal(s1[:, :k0], s3[:, :k0])
+
+
+def test_lse_matches_oracle_on_processed_rows():
+    _say("lse parity")
+    bt = make_batch([41, 42], [1500, 600], 8, 2, 128, heavy=True)
+    q, k, _ = to_device(bt)
+    a, b = [1.0, 0.0], [16, 1]
+    first = W.waits.first_rows(bt.cu_seqlens, a, b)
+    out = torch.full((8, bt.total_tokens), float("nan"), device=DEV)
+    W.lse(q, k, bt.cu_seqlens, a, b, out=out)
+    got = out.cpu().numpy()
+    rows = [np.arange(int(f), int(n)) for f, n in zip(first, bt.lengths)]
+    ref = orc.waits_lse(bt.q, bt.k, bt.cu_seqlens, 8, 2, float(np.float32(1 / math.sqrt(128))),
+                        rows_per_prompt=rows)
+    done = ~np.isnan(ref)
+    assert np.array_equal(~np.isnan(got), done)   # exactly the processed rows are written
+    np.testing.assert_allclose(got[done], ref[done], rtol=0, atol=2e-5 * np.abs(ref[done]).max())
+
+
+# ------------------------------------------------------- select / compact ---
+
+@pytest.mark.parametrize("n,budget", [(5000, 128), (20000, 256), (131072, 2048), (70, 128)])
+def test_select_on_arbitrary_scores(n, budget):
+    _say(f"select n={n}")
+    rng = np.random.default_rng(n)
+    s = rng.random((3, n)).astype(np.float32)
+    s[:, rng.integers(0, n, n // 3)] = np.float32(0.75)   # many exact ties
+    s[1] = np.float32(0.5)                                 # a head of all ties
+    s[2, :n // 2] = 0.0
+    idx = W.select(torch.from_numpy(s).to(DEV), [0, n], budget).cpu().numpy()
+    for h in range(3):
+        np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
+
+
+def test_compact_with_padding_slots():
+    _say("compact padding")
+    bt = make_batch([51, 52], [10, 300], 4, 2, 128, heavy=True)
+    _, k, v = to_device(bt)
+    idx = np.full((2, 2, 16), -1, dtype=np.int32)
+    idx[0, :, :10] = np.arange(10)
+    idx[1, 0] = np.sort(np.random.default_rng(0).choice(300, 16, replace=False))
+    idx[1, 1, :5] = [0, 1, 2, 298, 299]
+    kc, vc = W.compact(k, v, torch.from_numpy(idx).to(DEV), bt.cu_seqlens, 16)
+    check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, bt.cu_seqlens)

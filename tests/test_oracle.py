@@ -292,3 +292,16 @@ def test_compact_gathers_exact_bits():
     assert np.array_equal(kc[0, 0, 1], bt.k_bits[7, 0])
     assert np.array_equal(vc[0, 1, 3], bt.v_bits[6, 1])
     assert not kc[0, 0, 3].any() and not vc[0, 0, 3].any()
+
+
+def test_sampling_restrictions_keep_their_stated_bounds():
+    # row_min: exact for keys >= row_min; weight_floor: error <= G * N * floor
+    n, hq, hkv, d = 160, 4, 2, 16
+    q, k, cu = _prompt(n, hq, hkv, d, 81, heavy=True)
+    full = orc.waits_scores(q, k, cu, hq, hkv, [0.3], [9], F32(0.25))
+    tail = orc.waits_scores(q, k, cu, hq, hkv, [0.3], [9], F32(0.25), row_min=[100])
+    np.testing.assert_array_equal(tail[:, 100:], full[:, 100:])
+    floor = 1e-12
+    cut = orc.waits_scores(q, k, cu, hq, hkv, [0.3], [9], F32(0.25), weight_floor=floor)
+    assert np.all(np.abs(cut - full) <= 2 * n * floor)
+    assert np.any(cut != full)
