@@ -78,6 +78,56 @@ __device__ __forceinline__ void mma_tile(f32x16& acc, const u32x4* a,
   }
 }
 
+// Two independent tiles sharing one operand, MFMAs interleaved so neither
+// chain waits on its own previous result.  shared_is_a: the shared operand is
+// the A side (acc_t += S * X_t), else the B side (acc_t += X_t * S).
+template <typename T, int D, bool shared_is_a>
+__device__ __forceinline__ void mma_tile2(f32x16& acc0, f32x16& acc1, const u32x4* x0,
+                                          const u32x4* x1, const u32x4* sh) {
+  constexpr int NV = TileGeom<T, D>::NV;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const bf16x8 s = __builtin_bit_cast(bf16x8, sh[v]);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, x0[v]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, x1[v]);
+      if constexpr (shared_is_a) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s, a0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s, a1, acc1, 0, 0, 0);
+      } else {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, s, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, s, acc1, 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const f32x4 s = __builtin_bit_cast(f32x4, sh[v]);
+      const f32x4 a0 = __builtin_bit_cast(f32x4, x0[v]);
+      const f32x4 a1 = __builtin_bit_cast(f32x4, x1[v]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (shared_is_a) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(s[e], a0[e], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(s[e], a1[e], acc1, 0, 0, 0);
+        } else {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[e], s[e], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], s[e], acc1, 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Sum of 16 values as a balanced tree (short dependency chains).
+__device__ __forceinline__ float sum16(const float* p) {
+  const float a = (p[0] + p[1]) + (p[2] + p[3]);
+  const float b = (p[4] + p[5]) + (p[6] + p[7]);
+  const float c = (p[8] + p[9]) + (p[10] + p[11]);
+  const float d = (p[12] + p[13]) + (p[14] + p[15]);
+  return (a + b) + (c + d);
+}
+
 // Row index (within the 32-row A tile) of output register v for lane half hf.
 __device__ __forceinline__ constexpr int out_row(int v, int hf) {
   return 8 * (v >> 2) + 4 * hf + (v & 3);
@@ -89,6 +139,14 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Wait until every vector-memory load this wave issued has completed
+// (s_waitcnt vmcnt(0), expcnt and lgkmcnt left open), and keep the scheduler
+// from moving instructions across the wait.
+__device__ __forceinline__ void vm_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {

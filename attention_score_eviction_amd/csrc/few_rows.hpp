@@ -1,0 +1,377 @@
+// Both QK^T passes for sequences whose processed rows are few: when the G
+// query heads of a KV head have at most FR_ROWS packed rows in total (large
+// a: only the last rows carry weight), one workgroup holds every row of the
+// head in registers and streams K past them exactly once.
+//
+// Work item = (sequence, KV head h, key chunk).  8 waves; wave w owns packed
+// row tiles w and w + 8 (32 rows each, MFMA operand fragments in
+// registers).  32-key tiles of K flow HBM -> registers (a FR_RING-deep ring
+// of loads in flight) -> LDS (double buffer) -> every wave.
+//
+// Pass 1 (log-sum-exp, WAITS README introduction: the softmax normaliser of
+// every weighted row).  MFMA(A = K tile, B = Q rows): each lane owns one
+// query row and 16 keys per tile, so the row's running (reference, sum) pair
+// is in-lane.  The exponent reference is lazy: elements cost one fma, one
+// v_exp_f32 and one add against a fixed per-lane reference, and the
+// reference moves (with a rescale of the sum) only when a tile overflows the
+// sum past 2^64 or the lane has no reference yet -- a per-tile check instead
+// of a per-element max.  Exponent arithmetic is in log2 units
+// (scale * log2 e folded into the fma).
+//
+// Pass 2 (weighted column sums).  MFMA(A = Q rows, B = K tile): each lane
+// owns one key and 16 rows per tile; p = exp2(dot * scale*log2 e - off[row])
+// with off = lse * log2 e + log2(1 + exp(-a (q - c))) (w folded in, off =
+// +inf for rows whose fp32 weight is 0).  A tile's 32 key scores are complete
+// inside the workgroup (every row of the head is here): in-lane sums, one
+// exchange between lane halves, and an 8-wave sum through LDS in a fixed
+// order, written straight to the score array -- no partial buffers, no
+// atomics, bitwise reproducible.
+#pragma once
+
+#include "device_common.hpp"
+#include "kernel_args.hpp"
+
+namespace waits {
+
+constexpr int FR_WAVES = 8;
+constexpr int FR_THREADS = FR_WAVES * WAVE;
+constexpr int FR_TW = 2;                              // row tiles per wave
+constexpr int FR_ROWS = FR_WAVES * FR_TW * TILE;      // 512 packed rows
+constexpr int FR_RING = 4;                            // K tiles in flight
+
+struct FrArgs {
+  const void* q;
+  const void* k;
+  float* lse;                 // pass 1 out (single chunk) / pass 2 in: [Hq, T]
+  float2* part;               // pass 1 partials when a head's keys are split
+  float* scores;              // pass 2 out: [Hkv, T]
+  Strides st;
+  int64_t T;
+  int32_t G;
+  int32_t hkv;
+  float scale;
+  float scale_log2;
+  SeqTable tab;               // nc / kc: key chunks; first[]: items
+};
+
+template <typename T, int D, bool PASS2>
+__global__ void __launch_bounds__(FR_THREADS)
+few_rows_kernel(const FrArgs args) {
+  using Geo = TileGeom<T, D>;
+  constexpr int HALF = Geo::ROW_BYTES / 2;
+  constexpr int CPR = Geo::ROW_BYTES / 16;                 // 16-byte chunks per K row
+  constexpr int CHUNKS = TILE * CPR;                        // per K tile
+  constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;  // chunks per thread
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][Geo::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) float row_off[FR_ROWS];   // pass 2: exponent offsets
+  __shared__ __attribute__((aligned(16))) int row_q[FR_ROWS];       // row position (-1: padding)
+  __shared__ float red[2][FR_WAVES][TILE];                         // pass 2: per-wave key sums
+
+  const SeqTable& tab = args.tab;
+  const int item = blockIdx.x;
+  const int p = find_seq(tab.first, tab.nb, item);
+  const int local = item - tab.first[p];
+  const int hkv = args.hkv, G = args.G;
+  const int h = local % hkv;
+  const int chunk = local / hkv;
+  const int N = tab.n[p], q0 = tab.q0[p];
+  const int PR = G * (N - q0);
+  const int64_t tok0 = tab.tok0[p];
+  const int kbeg = chunk * tab.kc[p];
+  const int kend = min(kbeg + tab.kc[p], N);
+  const int ntiles = (kend - kbeg + TILE - 1) / TILE;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform branches
+  const int lane = tid & 63, col = lane & 31, hf = lane >> 5;
+  const unsigned char* qb = static_cast<const unsigned char*>(args.q);
+  const unsigned char* kb = static_cast<const unsigned char*>(args.k);
+  const float cl2 = args.scale_log2;
+
+  // Row table (and pass-2 exponent offsets): one thread per packed row.
+  {
+    const int r = tid;
+    int q = -1;
+    float off = INFINITY;
+    if (r < PR) {
+      const int j = r / G;
+      q = q0 + j;
+      if constexpr (PASS2) {
+        const int g = h * G + (r - j * G);
+        const float lse = args.lse[(int64_t)g * args.T + tok0 + q];
+        const float e = expf(-tab.a[p] * ((float)q - tab.c[p]));  // w = 1 / (1 + e)
+        off = fmaf(lse, LOG2E, log2f(1.f + e));
+      }
+    }
+    row_q[r] = q;
+    if constexpr (PASS2) row_off[r] = off;
+  }
+
+  // Stationary Q fragments: row tiles wave and wave + FR_WAVES.
+  u32x4 qf[FR_TW][Geo::NV];
+  int tlo[FR_TW], thi[FR_TW];
+  bool tval[FR_TW];
+  int qrow[FR_TW];
+#pragma unroll
+  for (int t = 0; t < FR_TW; ++t) {
+    const int r0 = (wave + t * FR_WAVES) * TILE;
+    tval[t] = r0 < PR;
+    tlo[t] = q0 + r0 / G;
+    thi[t] = q0 + (min(r0 + TILE, PR) - 1) / G;
+    const int r = r0 + col;
+    const bool ok = r < PR;
+    const int rc = ok ? r : PR - 1;  // loads stay unconditional (in-bounds address)
+    const int j = rc / G;
+    const int g = h * G + (rc - j * G);
+    const int q = q0 + j;
+    qrow[t] = ok ? q : -1;
+    const unsigned char* src =
+        qb + ((tok0 + q) * args.st.q_tok + (int64_t)g * args.st.q_head) * Geo::ELT + hf * HALF;
+#pragma unroll
+    for (int v = 0; v < Geo::NV; ++v) {
+      const u32x4 x = ld16(src + 16 * v);
+      qf[t][v] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // K staging: ring of FR_RING tiles in registers.  Every thread issues the
+  // same number of loads per tile, always from an in-bounds address (tiles
+  // past the end re-read the last tile, keys past the chunk re-read its last
+  // key); invalid data is replaced by zeros when the tile is committed to
+  // LDS.  A fixed load count lets the compiler wait for exactly the oldest
+  // tile instead of draining the ring.
+  u32x4 ring[FR_RING][SV];
+  auto issue = [&](int tile, u32x4* dst) {
+    const int kt0 = kbeg + min(tile, ntiles - 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const int cid = min(tid + i * FR_THREADS, CHUNKS - 1);
+      const int key = min(kt0 + cid / CPR, kend - 1);
+      dst[i] = ld16(kb + ((tok0 + key) * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT +
+                    (cid % CPR) * 16);
+    }
+  };
+  auto commit = [&](int buf, int tile, const u32x4* src) {
+    const int kt0 = kbeg + tile * TILE;
+#pragma unroll
+    for (int i = 0; i < SV; ++i) {
+      const int cid = tid + i * FR_THREADS;
+      if (cid < CHUNKS) {
+        const bool ok = kt0 + cid / CPR < kend;
+        st16(lds[buf] + (cid / CPR) * Geo::LDS_STRIDE + (cid % CPR) * 16,
+             ok ? src[i] : u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+  };
+
+  // pass-1 state (per lane, per row tile): log2-unit reference and sum
+  float mref[FR_TW], lsum[FR_TW];
+  // pass-2 state: this lane's rows' offsets
+  float off[FR_TW][16];
+#pragma unroll
+  for (int t = 0; t < FR_TW; ++t) {
+    mref[t] = -INFINITY;
+    lsum[t] = 0.f;
+  }
+
+  // Pass-1 state update from 16 exponentials of one row tile; moves the
+  // reference (rescaling the sum) when the sum overflows past 2^64, is NaN,
+  // or the lane has no reference yet.  x: the 16 logits (masked ones -inf).
+  auto p1_update = [&](int t, const float* x, const float* pv) {
+    const float ln = lsum[t] + sum16(pv);
+    if (ln < 0x1p64f) {
+      lsum[t] = ln;
+    } else {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
+      if (mx != -INFINITY) {
+        const float mnew = fmaxf(mref[t], mx * cl2);
+        float p2[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p2[v] = fast_exp2(fmaf(x[v], cl2, -mnew));
+        const float alpha = (mref[t] == -INFINITY) ? 0.f : fast_exp2(mref[t] - mnew);
+        lsum[t] = lsum[t] * alpha + sum16(p2);
+        mref[t] = mnew;
+      }
+    }
+  };
+
+  // Epilogue of a tile strictly below the causal diagonal of every row of
+  // this workgroup (no masks, no branches before the sums): it shares a
+  // basic block with the next tile's MFMAs so the two can co-issue.
+  auto epi_clean = [&](f32x16* acc, float& csum) {
+#pragma unroll
+    for (int t = 0; t < FR_TW; ++t) {
+      float pv[16];
+      if constexpr (PASS2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(acc[t][v], cl2, -off[t][v]));
+        csum += sum16(pv);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(acc[t][v], cl2, -mref[t]));
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = acc[t][v];
+        p1_update(t, x, pv);
+      }
+    }
+  };
+
+  // Epilogue of any other tile: chunk padding (skipped), tiles no row of a
+  // row tile can see (skipped), tiles crossing the diagonal (masked).
+  auto epi_general = [&](f32x16* acc, int j, float& csum) {
+    if (j >= ntiles) return;
+    const int ktj = kbeg + j * TILE;
+#pragma unroll
+    for (int t = 0; t < FR_TW; ++t) {
+      if (!tval[t] || ktj > thi[t]) continue;
+      const bool diag = ktj + TILE - 1 > tlo[t];
+      float pv[16];
+      if constexpr (PASS2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(acc[t][v], cl2, -off[t][v]));
+        if (diag) {
+          const int rbase = (wave + t * FR_WAVES) * TILE;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int4 qv = *reinterpret_cast<const int4*>(&row_q[rbase + 8 * jj + 4 * hf]);
+            const int qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ktj + col > qq[e]) pv[4 * jj + e] = 0.f;
+          }
+        }
+        csum += sum16(pv);
+      } else {
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = acc[t][v];
+        if (diag) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (ktj + out_row(v, hf) > qrow[t]) x[v] = -INFINITY;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(x[v], cl2, -mref[t]));
+        p1_update(t, x, pv);
+      }
+    }
+  };
+
+  auto read_k = [&](int buf, u32x4* kf) {
+    const unsigned char* krow = lds[buf] + col * Geo::LDS_STRIDE + hf * HALF;
+#pragma unroll
+    for (int v = 0; v < Geo::NV; ++v) kf[v] = ld16(krow + 16 * v);
+  };
+  auto mma_both = [&](f32x16* acc, const u32x4* kf) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+    mma_tile2<T, D, !PASS2>(acc[0], acc[1], qf[0], qf[1], kf);
+  };
+  auto flush = [&](int j) {  // pass 2: key scores of tile j from the per-wave sums
+    if (tid < TILE) {
+      const int key = kbeg + j * TILE + tid;
+      float sc = 0.f;
+#pragma unroll
+      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & 1][w][tid];
+      if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
+    }
+  };
+
+  // Q (and the row table's loads) complete before the K ring starts, so the
+  // loads in flight at the loop head are exactly the ring, oldest first --
+  // the same order every later iteration sees.
+  vm_wait_all();
+#pragma unroll
+  for (int s = 0; s < FR_RING; ++s) issue(s, ring[s]);
+  __syncthreads();  // row table visible
+  if constexpr (PASS2) {
+#pragma unroll
+    for (int t = 0; t < FR_TW; ++t) {
+      const int rbase = (wave + t * FR_WAVES) * TILE;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 ov = *reinterpret_cast<const f32x4*>(&row_off[rbase + 8 * jj + 4 * hf]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) off[t][4 * jj + e] = ov[e];
+      }
+    }
+  }
+  f32x16 acc[2][FR_TW];
+  u32x4 kf[Geo::NV];
+  commit(0, 0, ring[0]);
+  issue(FR_RING, ring[0]);
+  __syncthreads();
+  read_k(0, kf);
+  mma_both(acc[0], kf);  // tile 0
+  commit(1, 1, ring[1]);
+  issue(FR_RING + 1, ring[1]);
+  __syncthreads();
+
+  // Iteration it: MFMAs of tile it and the epilogue of tile it - 1, then
+  // stage tile it + 1.  The loop runs a multiple of FR_RING iterations with
+  // no early exit (tiles past the chunk do no arithmetic that is kept), so
+  // every unrolled step sees the same loads in flight and waits only for the
+  // oldest one.
+  const int ntiles_pad = (ntiles + FR_RING - 1) / FR_RING * FR_RING;
+  for (int it0 = 1; it0 < 1 + ntiles_pad; it0 += FR_RING) {
+#pragma unroll
+    for (int s = 0; s < FR_RING; ++s) {
+      const int it = it0 + s;
+      const int cur = (1 + s) & 1;  // == it & 1
+      const int j = it - 1;
+      const bool clean = j < ntiles && kbeg + j * TILE + TILE - 1 <= q0;
+      float csum = 0.f;
+      read_k(cur, kf);
+      if (clean) {
+        mma_both(acc[cur], kf);
+        epi_clean(acc[cur ^ 1], csum);
+      } else {
+        mma_both(acc[cur], kf);
+        epi_general(acc[cur ^ 1], j, csum);
+      }
+      if constexpr (PASS2) {
+        csum += wave_xor32(csum);
+        if (hf == 0) red[j & 1][wave][col] = csum;
+        if (j >= 1 && j - 1 < ntiles) flush(j - 1);
+      }
+      {
+        const int nxt = (2 + s) % FR_RING;  // == (it + 1) % FR_RING
+        commit(cur ^ 1, it + 1, ring[nxt]);
+        issue(it + 1 + FR_RING, ring[nxt]);
+      }
+      __syncthreads();
+    }
+  }
+
+  if constexpr (PASS2) {
+    if (ntiles == ntiles_pad) flush(ntiles - 1);  // last tile not yet flushed
+  } else {
+    const int nc = tab.nc[p];
+#pragma unroll
+    for (int t = 0; t < FR_TW; ++t) {
+      const float mo = wave_xor32(mref[t]);
+      const float lo = wave_xor32(lsum[t]);
+      const float mx = fmaxf(mref[t], mo);
+      float lt = 0.f;
+      if (mx != -INFINITY) {
+        lt = (mref[t] == -INFINITY ? 0.f : lsum[t] * fast_exp2(mref[t] - mx)) +
+             (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - mx));
+      }
+      if (hf == 0 && qrow[t] >= 0) {
+        const int r = (wave + t * FR_WAVES) * TILE + col;
+        const int j = r / G;
+        const int g = h * G + (r - j * G);
+        if (nc == 1) {
+          args.lse[(int64_t)g * args.T + tok0 + qrow[t]] = (mx + log2f(lt)) * LN2;
+        } else {
+          args.part[tab.ws0[p] + ((int64_t)h * FR_ROWS + r) * nc + chunk] = make_float2(mx, lt);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace waits

@@ -17,6 +17,7 @@ struct SeqTable {
   int32_t rg[MAXB];           // pass 1: row groups per KV head
   int32_t nc[MAXB];           // pass 1: key chunks per row group
   int32_t kc[MAXB];           // pass 1: keys per chunk (multiple of 32)
+  int32_t prow[MAXB];         // pass 1: packed-row pitch per KV head of the partials
   float a[MAXB];              // forgetting-curve slope
   float c[MAXB];              // N - b - 0.5 (exact in fp32)
   int64_t tok0[MAXB];         // first token of the sequence in the packed batch
@@ -48,7 +49,6 @@ struct CombineArgs {
   int64_t T;
   int32_t G;
   int32_t hkv;
-  int32_t wgrows;             // pass-1 rows per workgroup
   SeqTable tab;               // first[] counts (KV head, packed row) pairs
 };
 

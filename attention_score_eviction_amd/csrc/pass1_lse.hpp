@@ -160,7 +160,7 @@ lse_kernel(const LseArgs args) {
     __syncthreads();
   }
 
-  const int rgrows = tab.rg[p] * WGROWS;
+  const int rgrows = tab.prow[p];  // = row groups * WGROWS
 #pragma unroll
   for (int t = 0; t < SW; ++t) {
     const float mo = wave_xor32(m[t]);
@@ -203,7 +203,7 @@ lse_combine_kernel(const CombineArgs args) {
   const int q = q0 + j;
   const int nc = tab.nc[p];
   const int last = q / tab.kc[p];
-  const float2* pp = args.part + tab.ws0[p] + ((int64_t)h * tab.rg[p] * args.wgrows + r) * nc;
+  const float2* pp = args.part + tab.ws0[p] + ((int64_t)h * tab.prow[p] + r) * nc;
   float mx = -INFINITY;
   for (int c = 0; c <= last; ++c) mx = fmaxf(mx, pp[c].x);
   float lt = 0.f;

@@ -13,6 +13,7 @@
 #include "kernel_args.hpp"
 #include "pass1_lse.hpp"
 #include "pass2_colsum.hpp"
+#include "few_rows.hpp"
 #include "select_compact.hpp"
 
 namespace waits {
@@ -27,10 +28,13 @@ constexpr int NUM_CU = 256;
 constexpr int MAX_SEQ_LEN = (1 << 22) - 1;        // keeps N - b - 0.5 exact in fp32
 constexpr int MAX_B = 1 << 22;
 constexpr float LIVE_EXP_LIMIT = 89.0f;           // expf overflows above ~88.7228
+constexpr int FR_MIN_CHUNK = 256;                 // few-rows: shortest key chunk
 
 struct Seq {
   int n = 0, q0 = 0, pr = 0;
-  int rg = 0, nc = 1, kc = 32;
+  bool fr = false;            // both passes on the few-rows kernels
+  int rg = 0;                 // general pass 1: row groups per KV head
+  int nc = 1, kc = 32;        // key chunks (pass 1 split; few-rows: both passes)
   int64_t tok0 = 0;
   float a = 0.f, c = 0.f;
 };
@@ -92,9 +96,19 @@ int first_live_row(int n, float a, int32_t b) {
   return std::min(q, n - 1);
 }
 
+int round32(int x) { return (x + 31) / 32 * 32; }
+
+// Launch plan.  A sequence goes to the few-rows kernels when all packed rows
+// of a KV head fit one workgroup; their key ranges are cut into chunks until
+// the batch has about one workgroup per compute unit.  The other sequences
+// use the general kernels; their pass-1 key range is split only when row
+// groups alone give too few workgroups.
 std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b) {
   const int G = s->n_q_heads / s->n_kv_heads;
+  // fp32 inputs at head_dim 128 would not fit the few-rows register budget
+  const bool fr_ok = !(s->dtype == WAITS_F32 && s->head_dim == 128);
   std::vector<Seq> v(s->batch);
+  int64_t fr_units = 0, gen_rg = 0;
   for (int i = 0; i < s->batch; ++i) {
     Seq& q = v[i];
     q.n = (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]);
@@ -103,30 +117,42 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
     q.c = (float)q.n - (float)(b ? b[i] : 1) - 0.5f;
     q.q0 = a ? first_live_row(q.n, a[i], b[i]) : 0;
     q.pr = G * (q.n - q.q0);
-    q.rg = (q.pr + WGROWS1 - 1) / WGROWS1;
+    q.fr = fr_ok && q.n > 0 && q.pr <= FR_ROWS;
+    q.rg = q.fr ? 0 : (q.pr + WGROWS1 - 1) / WGROWS1;
     q.nc = 1;
-    q.kc = std::max(32, (q.n + 31) / 32 * 32);
+    q.kc = std::max(32, round32(q.n));
+    if (q.fr) fr_units += s->n_kv_heads;
+    else gen_rg += (int64_t)s->n_kv_heads * q.rg;
   }
-  // Split the key range when rows alone give too few workgroups.
-  int64_t total_rg = 0;
-  for (const Seq& q : v) total_rg += (int64_t)s->n_kv_heads * q.rg;
-  if (total_rg > 0 && total_rg < 2 * NUM_CU) {
-    const int want = (int)((4 * NUM_CU + total_rg - 1) / total_rg);
+  if (fr_units > 0) {
+    const int want = (int)std::max<int64_t>(1, (NUM_CU + fr_units - 1) / fr_units);
     for (Seq& q : v) {
-      if (q.n == 0) continue;
+      if (!q.fr) continue;
+      const int nc = std::max(1, std::min(want, (q.n + FR_MIN_CHUNK - 1) / FR_MIN_CHUNK));
+      q.kc = round32((q.n + nc - 1) / nc);
+      q.nc = (q.n + q.kc - 1) / q.kc;
+    }
+  }
+  if (gen_rg > 0 && gen_rg < 2 * NUM_CU) {
+    const int want = (int)((4 * NUM_CU + gen_rg - 1) / gen_rg);
+    for (Seq& q : v) {
+      if (q.fr || q.n == 0) continue;
       const int nc = std::max(1, std::min(want, (q.n + 511) / 512));
-      q.kc = ((q.n + nc - 1) / nc + 31) / 32 * 32;
+      q.kc = round32((q.n + nc - 1) / nc);
       q.nc = (q.n + q.kc - 1) / q.kc;
     }
   }
   return v;
 }
 
+// Pass-1 packed-row pitch of a sequence's partials (per KV head).
+int partial_rows(const Seq& q) { return q.fr ? FR_ROWS : q.rg * WGROWS1; }
+
 // Partial (float2) slots pass 1 needs for sequences [lo, hi).
 int64_t partial_slots(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
   int64_t tot = 0;
   for (int i = lo; i < hi; ++i)
-    if (v[i].nc > 1) tot += (int64_t)s->n_kv_heads * v[i].rg * WGROWS1 * v[i].nc;
+    if (v[i].nc > 1) tot += (int64_t)s->n_kv_heads * partial_rows(v[i]) * v[i].nc;
   return tot;
 }
 
@@ -142,7 +168,7 @@ size_t lse_buffer_bytes(const waits_shape* s) {
   return (bytes + 255) / 256 * 256;
 }
 
-void fill_table(SeqTable& t, const std::vector<Seq>& v, int lo, int hi) {
+void fill_table(SeqTable& t, const std::vector<Seq>& v, int lo, int hi, int hkv) {
   std::memset(&t, 0, sizeof(t));
   t.nb = hi - lo;
   for (int i = lo; i < hi; ++i) {
@@ -153,9 +179,15 @@ void fill_table(SeqTable& t, const std::vector<Seq>& v, int lo, int hi) {
     t.rg[j] = q.rg;
     t.nc[j] = q.nc;
     t.kc[j] = q.kc;
+    t.prow[j] = partial_rows(q);
     t.a[j] = q.a;
     t.c[j] = q.c;
     t.tok0[j] = q.tok0;
+  }
+  int64_t ws0 = 0;
+  for (int i = lo; i < hi; ++i) {
+    t.ws0[i - lo] = ws0;
+    if (v[i].nc > 1) ws0 += (int64_t)hkv * partial_rows(v[i]) * v[i].nc;
   }
 }
 
@@ -175,13 +207,63 @@ void launch_colsum(const ColsumArgs& args, int items, hipStream_t st) {
   hipLaunchKernelGGL((colsum_kernel<T, D, SW2>), dim3(items), dim3(NTHREADS), 0, st, args);
 }
 
+template <bool PASS2, typename T, int D>
+void launch_fr(const FrArgs& args, int items, hipStream_t st) {
+  hipLaunchKernelGGL((few_rows_kernel<T, D, PASS2>), dim3(items), dim3(FR_THREADS), 0, st, args);
+}
+
+template <bool PASS2>
+void dispatch_fr(const waits_shape* s, const FrArgs& args, int items, hipStream_t st) {
+  if (s->dtype == WAITS_BF16) {
+    if (s->head_dim == 64) launch_fr<PASS2, bf16_t, 64>(args, items, st);
+    else launch_fr<PASS2, bf16_t, 128>(args, items, st);
+  } else {
+    launch_fr<PASS2, float, 64>(args, items, st);  // fp32 only at head_dim 64 (see plan_seqs)
+  }
+}
+
+FrArgs fr_args(const waits_shape* s, const void* q, const void* k) {
+  FrArgs f;
+  std::memset(&f, 0, sizeof(f));
+  f.q = q;
+  f.k = k;
+  f.st = strides_of(s);
+  f.T = s->cu_seqlens[s->batch];
+  f.G = s->n_q_heads / s->n_kv_heads;
+  f.hkv = s->n_kv_heads;
+  f.scale = s->scale;
+  f.scale_log2 = s->scale * LOG2E;
+  return f;
+}
+
 int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, const int32_t* b,
             float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, a, b);
   if (ws_bytes < lse_ws_bytes(s, v) || (lse_ws_bytes(s, v) > 0 && !ws)) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;
+  const int hkv = s->n_kv_heads;
   for (int lo = 0; lo < s->batch; lo += MAXB) {
     const int hi = std::min(s->batch, lo + MAXB);
+    SeqTable tab;
+    fill_table(tab, v, lo, hi, hkv);
+
+    // few-rows sequences
+    FrArgs f = fr_args(s, q, k);
+    f.lse = lse;
+    f.part = static_cast<float2*>(ws);
+    f.tab = tab;
+    int fr_items = 0;
+    for (int i = lo; i < hi; ++i) {
+      f.tab.first[i - lo] = fr_items;
+      if (v[i].fr) fr_items += hkv * v[i].nc;
+    }
+    f.tab.first[hi - lo] = fr_items;
+    if (fr_items > 0) {
+      dispatch_fr<false>(s, f, fr_items, stream);
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+
+    // general sequences
     LseArgs args;
     args.q = q;
     args.k = k;
@@ -190,44 +272,42 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     args.st = strides_of(s);
     args.T = s->cu_seqlens[s->batch];
     args.G = G;
-    args.hkv = s->n_kv_heads;
+    args.hkv = hkv;
     args.scale = s->scale;
     args.scale_log2 = s->scale * LOG2E;
-    fill_table(args.tab, v, lo, hi);
+    args.tab = tab;
     int items = 0;
-    int64_t ws0 = 0;
     for (int i = lo; i < hi; ++i) {
       args.tab.first[i - lo] = items;
-      args.tab.ws0[i - lo] = ws0;
-      items += s->n_kv_heads * v[i].rg * v[i].nc;
-      if (v[i].nc > 1) ws0 += (int64_t)s->n_kv_heads * v[i].rg * WGROWS1 * v[i].nc;
+      if (!v[i].fr) items += hkv * v[i].rg * v[i].nc;
     }
     args.tab.first[hi - lo] = items;
-    if (items == 0) continue;
-    if (s->dtype == WAITS_BF16) {
-      if (s->head_dim == 64) launch_lse<bf16_t, 64>(args, items, stream);
-      else launch_lse<bf16_t, 128>(args, items, stream);
-    } else {
-      if (s->head_dim == 64) launch_lse<float, 64>(args, items, stream);
-      else launch_lse<float, 128>(args, items, stream);
-    }
-    if (launched() != WAITS_OK) return WAITS_EDEVICE;
-
-    if (ws0 > 0) {
-      CombineArgs cargs;
-      cargs.lse = lse;
-      cargs.part = static_cast<const float2*>(ws);
-      cargs.T = args.T;
-      cargs.G = G;
-      cargs.hkv = s->n_kv_heads;
-      cargs.wgrows = WGROWS1;
-      cargs.tab = args.tab;
-      int rows = 0;
-      for (int i = lo; i < hi; ++i) {
-        cargs.tab.first[i - lo] = rows;
-        if (v[i].nc > 1) rows += s->n_kv_heads * v[i].pr;
+    if (items > 0) {
+      if (s->dtype == WAITS_BF16) {
+        if (s->head_dim == 64) launch_lse<bf16_t, 64>(args, items, stream);
+        else launch_lse<bf16_t, 128>(args, items, stream);
+      } else {
+        if (s->head_dim == 64) launch_lse<float, 64>(args, items, stream);
+        else launch_lse<float, 128>(args, items, stream);
       }
-      cargs.tab.first[hi - lo] = rows;
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+
+    // merge split key ranges
+    CombineArgs cargs;
+    cargs.lse = lse;
+    cargs.part = static_cast<const float2*>(ws);
+    cargs.T = args.T;
+    cargs.G = G;
+    cargs.hkv = hkv;
+    cargs.tab = tab;
+    int rows = 0;
+    for (int i = lo; i < hi; ++i) {
+      cargs.tab.first[i - lo] = rows;
+      if (v[i].nc > 1) rows += hkv * v[i].pr;
+    }
+    cargs.tab.first[hi - lo] = rows;
+    if (rows > 0) {
       hipLaunchKernelGGL(lse_combine_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, cargs);
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
@@ -239,8 +319,27 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
                const float* a, const int32_t* b, float* scores, hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, a, b);
   const int G = s->n_q_heads / s->n_kv_heads;
+  const int hkv = s->n_kv_heads;
   for (int lo = 0; lo < s->batch; lo += MAXB) {
     const int hi = std::min(s->batch, lo + MAXB);
+    SeqTable tab;
+    fill_table(tab, v, lo, hi, hkv);
+
+    FrArgs f = fr_args(s, q, k);
+    f.lse = const_cast<float*>(lse);
+    f.scores = scores;
+    f.tab = tab;
+    int fr_items = 0;
+    for (int i = lo; i < hi; ++i) {
+      f.tab.first[i - lo] = fr_items;
+      if (v[i].fr) fr_items += hkv * v[i].nc;
+    }
+    f.tab.first[hi - lo] = fr_items;
+    if (fr_items > 0) {
+      dispatch_fr<true>(s, f, fr_items, stream);
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+
     ColsumArgs args;
     args.q = q;
     args.k = k;
@@ -249,24 +348,25 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
     args.st = strides_of(s);
     args.T = s->cu_seqlens[s->batch];
     args.G = G;
-    args.hkv = s->n_kv_heads;
+    args.hkv = hkv;
     args.scale_log2 = s->scale * LOG2E;
-    fill_table(args.tab, v, lo, hi);
+    args.tab = tab;
     int items = 0;
     for (int i = lo; i < hi; ++i) {
       args.tab.first[i - lo] = items;
-      items += s->n_kv_heads * ((v[i].n + WGKEYS2 - 1) / WGKEYS2);
+      if (!v[i].fr) items += hkv * ((v[i].n + WGKEYS2 - 1) / WGKEYS2);
     }
     args.tab.first[hi - lo] = items;
-    if (items == 0) continue;
-    if (s->dtype == WAITS_BF16) {
-      if (s->head_dim == 64) launch_colsum<bf16_t, 64>(args, items, stream);
-      else launch_colsum<bf16_t, 128>(args, items, stream);
-    } else {
-      if (s->head_dim == 64) launch_colsum<float, 64>(args, items, stream);
-      else launch_colsum<float, 128>(args, items, stream);
+    if (items > 0) {
+      if (s->dtype == WAITS_BF16) {
+        if (s->head_dim == 64) launch_colsum<bf16_t, 64>(args, items, stream);
+        else launch_colsum<bf16_t, 128>(args, items, stream);
+      } else {
+        if (s->head_dim == 64) launch_colsum<float, 64>(args, items, stream);
+        else launch_colsum<float, 128>(args, items, stream);
+      }
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
-    if (launched() != WAITS_OK) return WAITS_EDEVICE;
   }
   return WAITS_OK;
 }
@@ -374,7 +474,7 @@ int waits_select(const waits_shape* s, const float* scores, int32_t budget, int3
     args.T = s->cu_seqlens[s->batch];
     args.hkv = s->n_kv_heads;
     args.budget = budget;
-    fill_table(args.tab, v, lo, hi);
+    fill_table(args.tab, v, lo, hi, s->n_kv_heads);
     int gmax = 0;
     for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
     const dim3 grid((hi - lo) * s->n_kv_heads);
@@ -417,7 +517,7 @@ int waits_compact(const waits_shape* s, const void* k, const void* v, const int3
     args.hkv = s->n_kv_heads;
     args.budget = budget;
     args.elt = e;
-    fill_table(args.tab, sq, lo, hi);
+    fill_table(args.tab, sq, lo, hi, s->n_kv_heads);
     const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
     if (launched() != WAITS_OK) return WAITS_EDEVICE;

@@ -1,0 +1,276 @@
+"""Benchmark of the WAITS prefill KV-selection path on one MI355X.
+
+One step = the whole path (pass-1 row log-sum-exp, pass-2 weighted column
+sums, top-k select, K/V compaction) over one batch of synthetic inputs that
+are already resident in HBM.  Default workload: the Llama-3.1-8B layer shape
+(32 query heads, 8 KV heads, head_dim 128), 32 independently generated
+layers of N = 16384 prompt tokens, a = 1, b = 16, select_budget = 128, bf16.
+
+Prints one JSON line: prompt tokens/s per layer (= layers x tokens / step
+time), the dominant kernel's roofline fraction (per-kernel times from HIP
+events on the stream the library launches on), and the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 8b|1b|long|mistral]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import ACTIONS, make_batch, make_prompt  # noqa: E402
+
+METRIC = "prompt tokens/s per layer for WAITS score+select+compact; % bf16 MFMA peak"
+UNIT = "tokens/s/layer"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ORACLE_FLOPS = 2e10           # rough float64 oracle rate (GEMM + exp + masking), for sizing
+
+
+def workload(name: str):
+    """(description, heads, d, lengths, seeds, a, b, budget)."""
+    if name == "8b":
+        L, n = 32, 16384
+        return dict(desc="Llama-3.1-8B layer shape, 32 layers x N=16384, a=1 b=16, budget 128",
+                    hq=32, hkv=8, d=128, lengths=[n] * L, seeds=[1000 + i for i in range(L)],
+                    a=[1.0] * L, b=[16] * L, budget=128, layers=L)
+    if name == "1b":
+        return dict(desc="Llama-3.2-1B layer shape, N=4096, five actions as five sequences, budget 128",
+                    hq=32, hkv=8, d=64, lengths=[4096] * 5, seeds=[1] * 5,
+                    a=[x[0] for x in ACTIONS], b=[x[1] for x in ACTIONS], budget=128, layers=5)
+    if name == "long":
+        return dict(desc="Llama-3.1-8B layer shape, one layer N=131072, a=1 b=16, budget 2048",
+                    hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[1.0], b=[16],
+                    budget=2048, layers=1)
+    if name == "mistral":
+        rng = np.random.default_rng(3)
+        lengths = [int(x) for x in rng.integers(8192, 32768, endpoint=True, size=8)]
+        acts = rng.integers(0, 5, size=8)
+        return dict(desc="Mistral-7B shape, 8 ragged prompts in [8192, 32768], per-prompt actions, budget 256",
+                    hq=32, hkv=8, d=128, lengths=lengths, seeds=[3000 + i for i in range(8)],
+                    a=[ACTIONS[j][0] for j in acts], b=[ACTIONS[j][1] for j in acts],
+                    budget=256, layers=1)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def live_rows_fp32(n: int, a: float, b: int) -> np.ndarray:
+    """Rows whose fp32 forgetting-curve weight is nonzero (the work the
+    method must do; rows with weight exactly 0 add nothing)."""
+    a32 = np.float32(a)
+    c = np.float32(n) - np.float32(b) - np.float32(0.5)
+    with np.errstate(over="ignore", invalid="ignore"):
+        w = np.float32(1) / (np.float32(1) + np.exp(a32 * (c - np.arange(n, dtype=np.float32))))
+    return np.nonzero(w != 0)[0]
+
+
+def algorithmic_work(wl):
+    """Per-launch algorithmic flops of one QK^T pass and bytes of select/compact."""
+    flops_pass = 0.0
+    for n, a, b in zip(wl["lengths"], wl["a"], wl["b"]):
+        rows = live_rows_fp32(n, a, b)
+        flops_pass += 2.0 * wl["d"] * wl["hq"] * float(np.sum(rows + 1))
+    hkv, d, budget, B = wl["hkv"], wl["d"], wl["budget"], len(wl["lengths"])
+    T = sum(wl["lengths"])
+    select_bytes = hkv * T * 4 + B * hkv * budget * 4
+    compact_bytes = 2 * 2 * B * hkv * budget * d * 2 + B * hkv * budget * 4
+    return flops_pass, select_bytes, compact_bytes
+
+
+def make_inputs(wl, device):
+    import torch
+
+    hq, hkv, d = wl["hq"], wl["hkv"], wl["d"]
+    T = sum(wl["lengths"])
+    q = torch.empty((T, hq, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((T, hkv, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((T, hkv, d), dtype=torch.bfloat16, device=device)
+    cu = np.zeros(len(wl["lengths"]) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(wl["lengths"])
+
+    def one(i):
+        return i, make_prompt(wl["seeds"][i], wl["lengths"][i], hq, hkv, d,
+                              heavy=True, dtype="bf16", values=False)
+
+    workers = min(16, len(wl["lengths"]), os.cpu_count() or 1)
+    with ThreadPoolExecutor(workers) as ex:
+        for i, bt in ex.map(one, range(len(wl["lengths"]))):
+            lo, hi = int(cu[i]), int(cu[i + 1])
+            for dst, src in ((q, bt.q_bits), (k, bt.k_bits), (v, bt.v_bits)):
+                dst[lo:hi].copy_(torch.from_numpy(src).view(torch.bfloat16))
+    return q, k, v, cu
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The float64 oracle, as it stands, on a bounded sample: the first
+    sequence of the workload (all KV heads), timed on this host's cores."""
+    from oracle import waits_oracle as orc
+
+    n = wl["lengths"][0]
+    bt = make_prompt(wl["seeds"][0], n, wl["hq"], wl["hkv"], wl["d"], heavy=True, dtype="bf16")
+    heads = wl["hkv"]
+    # bound the sample: fewer KV heads if one sequence would run too long.
+    # The oracle visits every row whose float64 weight is nonzero.
+    w64 = orc.sigmoid_weights(n, wl["a"][0], wl["b"][0])
+    rows = np.nonzero(w64)[0]
+    est_s = 2.0 * wl["d"] * wl["hq"] * float(np.sum(rows + 1)) / ORACLE_FLOPS
+    if est_s > budget_s:
+        heads = max(1, int(wl["hkv"] * budget_s / est_s))
+    g = wl["hq"] // wl["hkv"]
+    qs = np.ascontiguousarray(bt.q[:, :heads * g])
+    ks = np.ascontiguousarray(bt.k[:, :heads])
+    vs = np.ascontiguousarray(bt.v_bits[:, :heads])
+    scale = float(np.float32(1 / math.sqrt(wl["d"])))
+    t0 = time.perf_counter()
+    s = orc.waits_scores(qs, ks, bt.cu_seqlens, heads * g, heads, wl["a"][:1], wl["b"][:1], scale)
+    idx = orc.waits_select(s, bt.cu_seqlens, heads, wl["budget"])
+    orc.waits_compact(bt.k_bits[:, :heads], vs, bt.cu_seqlens, idx)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+        blas = ",".join(sorted({x.get("internal_api", "?") for x in threadpool_info()}))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads, blas = 1, "unknown"
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    # tokens/s per layer, scaled from the sampled KV heads to the full layer
+    value = n / (dt * wl["hkv"] / heads)
+    return {"value": value, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0 of the workload (N={n}), {heads} of {wl['hkv']} KV heads, "
+                      f"float64 numpy oracle incl. select+compact, {dt:.2f} s wall, "
+                      f"scaled to all KV heads; BLAS={blas}; affinity={len(os.sched_getaffinity(0))}"
+                      f" cpus; {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8b", choices=["8b", "1b", "long", "mistral"])
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the WAITS path needs no collectives and this "
+              "build runs on a single MI355X; multi-GPU sharding is design-only.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_score_eviction_amd as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workload(args.workload)
+    t_gen = time.perf_counter()
+    q, k, v, cu = make_inputs(wl, dev)
+    t_gen = time.perf_counter() - t_gen
+    a, b, budget = wl["a"], wl["b"], wl["budget"]
+    T, hq, hkv, d = int(cu[-1]), wl["hq"], wl["hkv"], wl["d"]
+    B = len(wl["lengths"])
+
+    lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
+    ws_bytes = W.waits.lse_workspace_bytes(q, k, cu, a, b)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scores = torch.empty((hkv, T), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, hkv, budget), dtype=torch.int32, device=dev)
+    kc = torch.empty((B, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        W.lse(q, k, cu, a, b, out=lse, workspace=ws)
+        if e: e[1].record(stream)
+        W.colsum(q, k, lse, cu, a, b, out=scores)
+        if e: e[2].record(stream)
+        W.select(scores, cu, budget, out=idx)
+        if e: e[3].record(stream)
+        W.compact(k, v, idx, cu, budget, k_out=kc, v_out=vc)
+        if e: e[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    names = ["lse_kernel", "colsum_kernel", "select_kernel", "compact_kernel"]
+    per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+           for j, nm in enumerate(names)}  # ms per launch (pass 1 includes its combine, if any)
+
+    flops_pass, sel_bytes, cmp_bytes = algorithmic_work(wl)
+    tokens_layers = float(sum(wl["lengths"]))  # every sequence is one layer of one prompt
+    value = tokens_layers / (ms_step * 1e-3)
+
+    frac = {
+        "lse_kernel": flops_pass / (per["lse_kernel"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "colsum_kernel": flops_pass / (per["colsum_kernel"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "select_kernel": sel_bytes / (per["select_kernel"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "compact_kernel": cmp_bytes / (per["compact_kernel"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    dom = max(("lse_kernel", "colsum_kernel"), key=lambda nm: per[nm])
+    achieved = flops_pass / (per[dom] * 1e-3) / 1e12
+    passes_ms = per["lse_kernel"] + per["colsum_kernel"]
+    sc_ms = per["select_kernel"] + per["compact_kernel"]
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl["desc"], "sequences": B, "tokens_per_step": T,
+                   "q_heads": hq, "kv_heads": hkv, "head_dim": d, "select_budget": budget,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "passes_mfma_frac": 2 * flops_pass / (passes_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "select_compact_hbm_frac": (sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kernels_us": {nm: per[nm] * 1e3 for nm in names},
+        "kernel_frac": frac,
+        "algorithmic": {"flops_per_pass": flops_pass, "select_bytes": sel_bytes,
+                        "compact_bytes": cmp_bytes},
+        "input_gen_s": t_gen,
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
