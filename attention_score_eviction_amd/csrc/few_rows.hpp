@@ -5,8 +5,11 @@
 //
 // Work item = (sequence, KV head h, key chunk).  8 waves; wave w owns packed
 // row tiles w and w + 8 (32 rows each, MFMA operand fragments in
-// registers).  32-key tiles of K flow HBM -> registers (a FR_RING-deep ring
-// of loads in flight) -> LDS (double buffer) -> every wave.
+// registers).  K moves in stages of FR_SUB 32-key sub-tiles: HBM -> registers
+// (FR_RING stages of loads in flight) -> LDS (double buffer, one barrier per
+// stage) -> every wave.  Each wave issues the MFMAs of sub-tile g in the same
+// basic block as the exponential epilogue of sub-tile g - 1, so the matrix
+// and vector pipes work side by side.
 //
 // Pass 1 (log-sum-exp, WAITS README introduction: the softmax normaliser of
 // every weighted row).  MFMA(A = K tile, B = Q rows): each lane owns one
@@ -33,11 +36,10 @@
 
 namespace waits {
 
-constexpr int FR_WAVES = 8;
-constexpr int FR_THREADS = FR_WAVES * WAVE;
-constexpr int FR_TW = 2;                              // row tiles per wave
-constexpr int FR_ROWS = FR_WAVES * FR_TW * TILE;      // 512 packed rows
-constexpr int FR_RING = 4;                            // K tiles in flight
+constexpr int FR_ROWS = 512;                          // packed rows per workgroup
+constexpr int FR_SUB = 2;                             // 32-key sub-tiles per stage
+constexpr int FR_STAGE = FR_SUB * TILE;               // keys per stage (one barrier)
+constexpr int FR_RING = 2;                            // stages of loads in flight
 
 struct FrArgs {
   const void* q;
@@ -54,18 +56,22 @@ struct FrArgs {
   SeqTable tab;               // nc / kc: key chunks; first[]: items
 };
 
-template <typename T, int D, bool PASS2>
-__global__ void __launch_bounds__(FR_THREADS)
+// FR_WAVES waves, each owning FR_TW row tiles (FR_WAVES * FR_TW * 32 == FR_ROWS).
+template <typename T, int D, bool PASS2, int FR_WAVES, int FR_TW>
+__global__ void __launch_bounds__(FR_WAVES * WAVE)
 few_rows_kernel(const FrArgs args) {
+  constexpr int FR_THREADS = FR_WAVES * WAVE;
+  static_assert(FR_WAVES * FR_TW * TILE == FR_ROWS, "one workgroup holds FR_ROWS rows");
   using Geo = TileGeom<T, D>;
   constexpr int HALF = Geo::ROW_BYTES / 2;
-  constexpr int CPR = Geo::ROW_BYTES / 16;                 // 16-byte chunks per K row
-  constexpr int CHUNKS = TILE * CPR;                        // per K tile
-  constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;  // chunks per thread
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][Geo::LDS_BYTES];
+  constexpr int CPR = Geo::ROW_BYTES / 16;                    // 16-byte chunks per K row
+  constexpr int CHUNKS = FR_STAGE * CPR;                       // per stage
+  constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;   // chunks per thread per stage
+  static_assert(FR_SUB == 2, "accumulator parity follows the sub-tile index");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float row_off[FR_ROWS];   // pass 2: exponent offsets
   __shared__ __attribute__((aligned(16))) int row_q[FR_ROWS];       // row position (-1: padding)
-  __shared__ float red[2][FR_WAVES][TILE];                         // pass 2: per-wave key sums
+  __shared__ float red[4][FR_WAVES][TILE];                         // pass 2: per-wave key sums
 
   const SeqTable& tab = args.tab;
   const int item = blockIdx.x;
@@ -79,7 +85,8 @@ few_rows_kernel(const FrArgs args) {
   const int64_t tok0 = tab.tok0[p];
   const int kbeg = chunk * tab.kc[p];
   const int kend = min(kbeg + tab.kc[p], N);
-  const int ntiles = (kend - kbeg + TILE - 1) / TILE;
+  const int nsub = (kend - kbeg + TILE - 1) / TILE;     // 32-key sub-tiles
+  const int nst = (nsub + FR_SUB - 1) / FR_SUB;          // stages
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform branches
@@ -89,8 +96,7 @@ few_rows_kernel(const FrArgs args) {
   const float cl2 = args.scale_log2;
 
   // Row table (and pass-2 exponent offsets): one thread per packed row.
-  {
-    const int r = tid;
+  for (int r = tid; r < FR_ROWS; r += FR_THREADS) {
     int q = -1;
     float off = INFINITY;
     if (r < PR) {
@@ -134,31 +140,33 @@ few_rows_kernel(const FrArgs args) {
     }
   }
 
-  // K staging: ring of FR_RING tiles in registers.  Every thread issues the
-  // same number of loads per tile, always from an in-bounds address (tiles
-  // past the end re-read the last tile, keys past the chunk re-read its last
-  // key); invalid data is replaced by zeros when the tile is committed to
-  // LDS.  A fixed load count lets the compiler wait for exactly the oldest
-  // tile instead of draining the ring.
+  // K staging: ring of FR_RING stages in registers.  Every thread issues the
+  // same number of loads per stage, always from an in-bounds address (stages
+  // past the end re-read the last one, rows past the sequence re-read its
+  // last key); rows outside the chunk become zeros when a stage is committed
+  // to LDS.  A fixed load count lets the compiler wait for exactly the oldest
+  // stage instead of draining the ring.
+  const int64_t row_bytes = args.st.kv_tok * Geo::ELT;
+  const unsigned char* kseq = kb + (tok0 * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT;
   u32x4 ring[FR_RING][SV];
-  auto issue = [&](int tile, u32x4* dst) {
-    const int kt0 = kbeg + min(tile, ntiles - 1) * TILE;
+  auto issue = [&](int stage, u32x4* dst) {
+    const int k0 = kbeg + min(stage, nst - 1) * FR_STAGE;
 #pragma unroll
     for (int i = 0; i < SV; ++i) {
       const int cid = min(tid + i * FR_THREADS, CHUNKS - 1);
-      const int key = min(kt0 + cid / CPR, kend - 1);
-      dst[i] = ld16(kb + ((tok0 + key) * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT +
-                    (cid % CPR) * 16);
+      const int key = min(k0 + cid / CPR, N - 1);
+      dst[i] = ld16(kseq + key * row_bytes + (cid % CPR) * 16);
     }
   };
-  auto commit = [&](int buf, int tile, const u32x4* src) {
-    const int kt0 = kbeg + tile * TILE;
+  auto commit = [&](int buf, int stage, const u32x4* src) {
+    const int k0 = kbeg + stage * FR_STAGE;
 #pragma unroll
     for (int i = 0; i < SV; ++i) {
       const int cid = tid + i * FR_THREADS;
       if (cid < CHUNKS) {
-        const bool ok = kt0 + cid / CPR < kend;
-        st16(lds[buf] + (cid / CPR) * Geo::LDS_STRIDE + (cid % CPR) * 16,
+        const int row = cid / CPR;
+        const bool ok = k0 + row < kend;
+        st16(lds[buf][row / TILE] + (row % TILE) * Geo::LDS_STRIDE + (cid % CPR) * 16,
              ok ? src[i] : u32x4{0u, 0u, 0u, 0u});
       }
     }
@@ -197,9 +205,8 @@ few_rows_kernel(const FrArgs args) {
     }
   };
 
-  // Epilogue of a tile strictly below the causal diagonal of every row of
-  // this workgroup (no masks, no branches before the sums): it shares a
-  // basic block with the next tile's MFMAs so the two can co-issue.
+  // Epilogue of a sub-tile strictly below the causal diagonal of every row of
+  // this workgroup (no masks, no branches before the sums).
   auto epi_clean = [&](f32x16* acc, float& csum) {
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
@@ -219,10 +226,10 @@ few_rows_kernel(const FrArgs args) {
     }
   };
 
-  // Epilogue of any other tile: chunk padding (skipped), tiles no row of a
-  // row tile can see (skipped), tiles crossing the diagonal (masked).
+  // Epilogue of any other sub-tile: chunk padding (skipped), sub-tiles no row
+  // of a row tile can see (skipped), sub-tiles crossing the diagonal (masked).
   auto epi_general = [&](f32x16* acc, int j, float& csum) {
-    if (j >= ntiles) return;
+    if (j < 0 || j >= nsub) return;
     const int ktj = kbeg + j * TILE;
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
@@ -260,23 +267,52 @@ few_rows_kernel(const FrArgs args) {
     }
   };
 
-  auto read_k = [&](int buf, u32x4* kf) {
-    const unsigned char* krow = lds[buf] + col * Geo::LDS_STRIDE + hf * HALF;
+  auto read_k = [&](int buf, int u, u32x4* kf) {
+    const unsigned char* krow = lds[buf][u] + col * Geo::LDS_STRIDE + hf * HALF;
 #pragma unroll
     for (int v = 0; v < Geo::NV; ++v) kf[v] = ld16(krow + 16 * v);
   };
   auto mma_both = [&](f32x16* acc, const u32x4* kf) {
-    acc[0] = f32x16{};
-    acc[1] = f32x16{};
-    mma_tile2<T, D, !PASS2>(acc[0], acc[1], qf[0], qf[1], kf);
+#pragma unroll
+    for (int t = 0; t < FR_TW; t += 2) {
+      acc[t] = f32x16{};
+      acc[t + 1] = f32x16{};
+      mma_tile2<T, D, !PASS2>(acc[t], acc[t + 1], qf[t], qf[t + 1], kf);
+    }
   };
-  auto flush = [&](int j) {  // pass 2: key scores of tile j from the per-wave sums
-    if (tid < TILE) {
+  // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)
+  auto red_store = [&](int j, float csum) {
+    csum += wave_xor32(csum);
+    if (hf == 0) red[j & 3][wave][col] = csum;
+  };
+  auto flush = [&](int j) {
+    if (j >= 0 && j < nsub && tid < TILE) {
       const int key = kbeg + j * TILE + tid;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & 1][w][tid];
+      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & 3][w][tid];
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
+    }
+  };
+
+  // Sub-tile g: MFMAs into acc[g & 1] in the same block as the epilogue of
+  // sub-tile g - 1 from acc[(g - 1) & 1].
+  f32x16 acc[2][FR_TW];
+  u32x4 kf[Geo::NV];
+  auto subtile = [&](int buf, int u, int g) {
+    const int j = g - 1;
+    const bool clean = j >= 0 && j < nsub && kbeg + j * TILE + TILE - 1 <= q0;
+    float csum = 0.f;
+    read_k(buf, u, kf);
+    if (clean) {
+      mma_both(acc[u & 1], kf);
+      epi_clean(acc[(u & 1) ^ 1], csum);
+    } else {
+      mma_both(acc[u & 1], kf);
+      epi_general(acc[(u & 1) ^ 1], j, csum);
+    }
+    if constexpr (PASS2) {
+      if (j >= 0) red_store(j, csum);
     }
   };
 
@@ -299,55 +335,44 @@ few_rows_kernel(const FrArgs args) {
       }
     }
   }
-  f32x16 acc[2][FR_TW];
-  u32x4 kf[Geo::NV];
   commit(0, 0, ring[0]);
   issue(FR_RING, ring[0]);
   __syncthreads();
-  read_k(0, kf);
-  mma_both(acc[0], kf);  // tile 0
+#pragma unroll
+  for (int u = 0; u < FR_SUB; ++u) subtile(0, u, u);  // stage 0
   commit(1, 1, ring[1]);
   issue(FR_RING + 1, ring[1]);
   __syncthreads();
 
-  // Iteration it: MFMAs of tile it and the epilogue of tile it - 1, then
-  // stage tile it + 1.  The loop runs a multiple of FR_RING iterations with
-  // no early exit (tiles past the chunk do no arithmetic that is kept), so
-  // every unrolled step sees the same loads in flight and waits only for the
-  // oldest one.
-  const int ntiles_pad = (ntiles + FR_RING - 1) / FR_RING * FR_RING;
-  for (int it0 = 1; it0 < 1 + ntiles_pad; it0 += FR_RING) {
+  // Stage st: sub-tiles st*FR_SUB + u, then stage st + 1 goes to LDS.  The
+  // loop runs a multiple of FR_RING stages with no early exit (stages past
+  // the chunk do no arithmetic that is kept), so every unrolled step sees the
+  // same loads in flight and waits only for the oldest stage.
+  const int nst_pad = (nst + FR_RING - 1) / FR_RING * FR_RING;
+  for (int st0 = 1; st0 < 1 + nst_pad; st0 += FR_RING) {
 #pragma unroll
     for (int s = 0; s < FR_RING; ++s) {
-      const int it = it0 + s;
-      const int cur = (1 + s) & 1;  // == it & 1
-      const int j = it - 1;
-      const bool clean = j < ntiles && kbeg + j * TILE + TILE - 1 <= q0;
-      float csum = 0.f;
-      read_k(cur, kf);
-      if (clean) {
-        mma_both(acc[cur], kf);
-        epi_clean(acc[cur ^ 1], csum);
-      } else {
-        mma_both(acc[cur], kf);
-        epi_general(acc[cur ^ 1], j, csum);
-      }
+      const int st = st0 + s;
+      const int buf = (1 + s) & 1;  // == st & 1
       if constexpr (PASS2) {
-        csum += wave_xor32(csum);
-        if (hf == 0) red[j & 1][wave][col] = csum;
-        if (j >= 1 && j - 1 < ntiles) flush(j - 1);
+#pragma unroll
+        for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 3);  // previous stage's epilogues
       }
+#pragma unroll
+      for (int u = 0; u < FR_SUB; ++u) subtile(buf, u, st * FR_SUB + u);
       {
-        const int nxt = (2 + s) % FR_RING;  // == (it + 1) % FR_RING
-        commit(cur ^ 1, it + 1, ring[nxt]);
-        issue(it + 1 + FR_RING, ring[nxt]);
+        const int nxt = (2 + s) % FR_RING;  // == (st + 1) % FR_RING
+        commit(buf ^ 1, st + 1, ring[nxt]);
+        issue(st + 1 + FR_RING, ring[nxt]);
       }
       __syncthreads();
     }
   }
 
   if constexpr (PASS2) {
-    if (ntiles == ntiles_pad) flush(ntiles - 1);  // last tile not yet flushed
+    const int st = nst_pad;  // epilogues of the last stage
+#pragma unroll
+    for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 1);
   } else {
     const int nc = tab.nc[p];
 #pragma unroll

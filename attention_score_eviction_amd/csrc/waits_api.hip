@@ -207,9 +207,13 @@ void launch_colsum(const ColsumArgs& args, int items, hipStream_t st) {
   hipLaunchKernelGGL((colsum_kernel<T, D, SW2>), dim3(items), dim3(NTHREADS), 0, st, args);
 }
 
+constexpr int FRW = 8;  // few-rows waves per workgroup
+constexpr int FRT = FR_ROWS / (FRW * TILE);
+
 template <bool PASS2, typename T, int D>
 void launch_fr(const FrArgs& args, int items, hipStream_t st) {
-  hipLaunchKernelGGL((few_rows_kernel<T, D, PASS2>), dim3(items), dim3(FR_THREADS), 0, st, args);
+  hipLaunchKernelGGL((few_rows_kernel<T, D, PASS2, FRW, FRT>), dim3(items), dim3(FRW * WAVE), 0, st,
+                     args);
 }
 
 template <bool PASS2>

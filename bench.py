@@ -35,7 +35,6 @@ METRIC = "prompt tokens/s per layer for WAITS score+select+compact; % bf16 MFMA 
 UNIT = "tokens/s/layer"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ORACLE_FLOPS = 2e10           # rough float64 oracle rate (GEMM + exp + masking), for sizing
 
 
 def workload(name: str):
@@ -112,34 +111,34 @@ def make_inputs(wl, device):
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The float64 oracle, as it stands, on a bounded sample: the first
-    sequence of the workload (all KV heads), timed on this host's cores."""
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    whole sequences (all KV heads), taken in order until about ``budget_s``
+    seconds of CPU work have run (at least one), timed on this host's cores.
+    Reported in the GPU's unit: sequence tokens per second (one sequence =
+    one layer of one prompt)."""
     from oracle import waits_oracle as orc
 
-    n = wl["lengths"][0]
-    bt = make_prompt(wl["seeds"][0], n, wl["hq"], wl["hkv"], wl["d"], heavy=True, dtype="bf16")
-    heads = wl["hkv"]
-    # bound the sample: fewer KV heads if one sequence would run too long.
-    # The oracle visits every row whose float64 weight is nonzero.
-    w64 = orc.sigmoid_weights(n, wl["a"][0], wl["b"][0])
-    rows = np.nonzero(w64)[0]
-    est_s = 2.0 * wl["d"] * wl["hq"] * float(np.sum(rows + 1)) / ORACLE_FLOPS
-    if est_s > budget_s:
-        heads = max(1, int(wl["hkv"] * budget_s / est_s))
-    g = wl["hq"] // wl["hkv"]
-    qs = np.ascontiguousarray(bt.q[:, :heads * g])
-    ks = np.ascontiguousarray(bt.k[:, :heads])
-    vs = np.ascontiguousarray(bt.v_bits[:, :heads])
     scale = float(np.float32(1 / math.sqrt(wl["d"])))
-    t0 = time.perf_counter()
-    s = orc.waits_scores(qs, ks, bt.cu_seqlens, heads * g, heads, wl["a"][:1], wl["b"][:1], scale)
-    idx = orc.waits_select(s, bt.cu_seqlens, heads, wl["budget"])
-    orc.waits_compact(bt.k_bits[:, :heads], vs, bt.cu_seqlens, idx)
-    dt = time.perf_counter() - t0
+    done_tokens, spent, used = 0, 0.0, 0
+    for i in range(len(wl["lengths"])):
+        n = wl["lengths"][i]
+        bt = make_prompt(wl["seeds"][i], n, wl["hq"], wl["hkv"], wl["d"], heavy=True, dtype="bf16")
+        t0 = time.perf_counter()
+        s = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, wl["hq"], wl["hkv"], wl["a"][i:i + 1],
+                             wl["b"][i:i + 1], scale)
+        idx = orc.waits_select(s, bt.cu_seqlens, wl["hkv"], wl["budget"])
+        orc.waits_compact(bt.k_bits, bt.v_bits, bt.cu_seqlens, idx)
+        spent += time.perf_counter() - t0
+        done_tokens += n
+        used += 1
+        if spent >= budget_s:
+            break
     try:
         from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-        blas = ",".join(sorted({x.get("internal_api", "?") for x in threadpool_info()}))
+        info = threadpool_info()
+        threads = max([x.get("num_threads", 1) for x in info] or [1])
+        blas = ",".join(sorted({f"{x.get('internal_api', '?')}x{x.get('num_threads', '?')}"
+                                for x in info}))
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads, blas = 1, "unknown"
     cpu = "unknown"
@@ -151,13 +150,53 @@ def cpu_baseline(wl, budget_s: float):
                     break
     except OSError:
         pass
-    # tokens/s per layer, scaled from the sampled KV heads to the full layer
-    value = n / (dt * wl["hkv"] / heads)
-    return {"value": value, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"sequence 0 of the workload (N={n}), {heads} of {wl['hkv']} KV heads, "
-                      f"float64 numpy oracle incl. select+compact, {dt:.2f} s wall, "
-                      f"scaled to all KV heads; BLAS={blas}; affinity={len(os.sched_getaffinity(0))}"
-                      f" cpus; {cpu}"}
+    return {"value": done_tokens / spent, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"first {used} of {len(wl['lengths'])} sequences of the workload "
+                      f"({done_tokens} tokens, all {wl['hkv']} KV heads), float64 numpy oracle "
+                      f"incl. select+compact, {spent:.1f} s; BLAS {blas}; "
+                      f"{len(os.sched_getaffinity(0))} cpus in affinity; {cpu}"}
+
+
+KERNEL_SOURCES = ("attention_score_eviction_amd/csrc/few_rows.hpp",
+                  "attention_score_eviction_amd/csrc/device_common.hpp",
+                  "attention_score_eviction_amd/csrc/kernel_args.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload_name: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter record
+    (profiles/traffic_<workload>.json), or None when there is none or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of a known size, for scaling the HBM
+    byte counters (each launch reads and writes ``nbytes``)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -168,7 +207,12 @@ def main():
     ap.add_argument("--workload", default="8b", choices=["8b", "1b", "long", "mistral"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the WAITS path needs no collectives and this "
               "build runs on a single MI355X; multi-GPU sharding is design-only.",
@@ -220,7 +264,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    names = ["lse_kernel", "colsum_kernel", "select_kernel", "compact_kernel"]
+    names = ["pass1_lse", "pass2_colsum", "select", "compact"]
     per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            for j, nm in enumerate(names)}  # ms per launch (pass 1 includes its combine, if any)
 
@@ -229,15 +273,15 @@ def main():
     value = tokens_layers / (ms_step * 1e-3)
 
     frac = {
-        "lse_kernel": flops_pass / (per["lse_kernel"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "colsum_kernel": flops_pass / (per["colsum_kernel"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "select_kernel": sel_bytes / (per["select_kernel"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "compact_kernel": cmp_bytes / (per["compact_kernel"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "pass1_lse": flops_pass / (per["pass1_lse"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "pass2_colsum": flops_pass / (per["pass2_colsum"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "select": sel_bytes / (per["select"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "compact": cmp_bytes / (per["compact"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
-    dom = max(("lse_kernel", "colsum_kernel"), key=lambda nm: per[nm])
+    dom = max(("pass1_lse", "pass2_colsum"), key=lambda nm: per[nm])
     achieved = flops_pass / (per[dom] * 1e-3) / 1e12
-    passes_ms = per["lse_kernel"] + per["colsum_kernel"]
-    sc_ms = per["select_kernel"] + per["compact_kernel"]
+    passes_ms = per["pass1_lse"] + per["pass2_colsum"]
+    sc_ms = per["select"] + per["compact"]
 
     out = {
         "metric": METRIC,
@@ -257,7 +301,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(dom, args.workload)},
         "passes_mfma_frac": 2 * flops_pass / (passes_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "select_compact_hbm_frac": (sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels_us": {nm: per[nm] * 1e3 for nm in names},
