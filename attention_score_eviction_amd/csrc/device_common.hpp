@@ -39,6 +39,11 @@ constexpr int NTHREADS = NWAVES * WAVE;
 constexpr int TILE = 32;  // rows of an MFMA operand tile
 constexpr int MAXB = 32;  // sequences per launch (tables travel as kernel arguments)
 
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts:
+// 32-bit data format, so untyped loads return data and reads at or past
+// num_records bytes return zeros.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 

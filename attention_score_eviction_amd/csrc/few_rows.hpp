@@ -140,34 +140,41 @@ few_rows_kernel(const FrArgs args) {
     }
   }
 
-  // K staging: ring of FR_RING stages in registers.  Every thread issues the
-  // same number of loads per stage, always from an in-bounds address (stages
-  // past the end re-read the last one, rows past the sequence re-read its
-  // last key); rows outside the chunk become zeros when a stage is committed
-  // to LDS.  A fixed load count lets the compiler wait for exactly the oldest
-  // stage instead of draining the ring.
-  const int64_t row_bytes = args.st.kv_tok * Geo::ELT;
+  // K staging: ring of FR_RING stages in registers, fetched with buffer loads
+  // over this sequence's rows of head h: one 32-bit offset add per load, and
+  // the hardware range check returns zeros past the sequence (the host sends
+  // a sequence here only when its K span fits 2^31 bytes).  Stages past the
+  // chunk re-read its last stage, so every thread issues the same number of
+  // loads per stage and the compiler waits for exactly the oldest stage.
+  // Rows past the chunk but inside the sequence carry real keys; they are
+  // never used: sub-tiles are 32-key aligned with the chunk end, sub-tiles
+  // past it skip their epilogue, and keys past the sequence are causal-masked
+  // (pass 1) or not written (pass 2).
+  const int row_bytes = (int)(args.st.kv_tok * Geo::ELT);
   const unsigned char* kseq = kb + (tok0 * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kseq), 0, N * row_bytes, BUFFER_RSRC_WORD3);
+  int voff[SV];
+#pragma unroll
+  for (int i = 0; i < SV; ++i) {
+    const int cid = min(tid + i * FR_THREADS, CHUNKS - 1);
+    voff[i] = (cid / CPR) * row_bytes + (cid % CPR) * 16;
+  }
   u32x4 ring[FR_RING][SV];
   auto issue = [&](int stage, u32x4* dst) {
-    const int k0 = kbeg + min(stage, nst - 1) * FR_STAGE;
+    const int sbase = (kbeg + min(stage, nst - 1) * FR_STAGE) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < SV; ++i) {
-      const int cid = min(tid + i * FR_THREADS, CHUNKS - 1);
-      const int key = min(k0 + cid / CPR, N - 1);
-      dst[i] = ld16(kseq + key * row_bytes + (cid % CPR) * 16);
-    }
+    for (int i = 0; i < SV; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i] + sbase, 0, 0));
   };
   auto commit = [&](int buf, int stage, const u32x4* src) {
-    const int k0 = kbeg + stage * FR_STAGE;
+    (void)stage;
 #pragma unroll
     for (int i = 0; i < SV; ++i) {
       const int cid = tid + i * FR_THREADS;
       if (cid < CHUNKS) {
         const int row = cid / CPR;
-        const bool ok = k0 + row < kend;
-        st16(lds[buf][row / TILE] + (row % TILE) * Geo::LDS_STRIDE + (cid % CPR) * 16,
-             ok ? src[i] : u32x4{0u, 0u, 0u, 0u});
+        st16(lds[buf][row / TILE] + (row % TILE) * Geo::LDS_STRIDE + (cid % CPR) * 16, src[i]);
       }
     }
   };
@@ -303,11 +310,12 @@ few_rows_kernel(const FrArgs args) {
     const int j = g - 1;
     const bool clean = j >= 0 && j < nsub && kbeg + j * TILE + TILE - 1 <= q0;
     float csum = 0.f;
-    read_k(buf, u, kf);
     if (clean) {
+      read_k(buf, u, kf);
       mma_both(acc[u & 1], kf);
       epi_clean(acc[(u & 1) ^ 1], csum);
     } else {
+      read_k(buf, u, kf);
       mma_both(acc[u & 1], kf);
       epi_general(acc[(u & 1) ^ 1], j, csum);
     }

@@ -53,6 +53,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
   return out;
 }
 
+// hist[d] += 1 for every active lane whose value matches; lanes that agree
+// with the wave's first candidate digit are counted with one atomic (the
+// leading radix digits of similar-magnitude scores are shared by almost all
+// keys, so per-lane atomics would serialise on one LDS word).
+__device__ __forceinline__ void hist_add(int* hist, bool take, uint32_t d) {
+  const uint64_t cand = __ballot(take);
+  if (cand == 0) return;
+  const int leader = __builtin_ctzll(cand);
+  const uint32_t ld = __shfl(d, leader, 64);
+  const uint64_t same = __ballot(take && d == ld);
+  const int lane = threadIdx.x & 63;
+  if (lane == leader) atomicAdd(&hist[ld], __builtin_popcountll(same));
+  else if (take && d != ld) atomicAdd(&hist[d], 1);
+}
+
 template <int PTC>
 __global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs args) {
@@ -76,13 +91,23 @@ select_kernel(const SelectArgs args) {
   }
   const uint32_t* s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)h * args.T + tab.tok0[p]);
 
-  const int per = (N + SEL_THREADS - 1) / SEL_THREADS;
+  const int per = ((N + SEL_THREADS - 1) / SEL_THREADS + 3) & ~3;  // multiple of 4
   const int beg = min(tid * per, N);
   const int cnt = min(per, N - beg);
   uint32_t cache[PTC > 0 ? PTC : 1];
+  // runs start at multiples of 4 scores: 16-byte aligned when the head's row is
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;
   if constexpr (PTC > 0) {
 #pragma unroll
-    for (int i = 0; i < PTC; ++i) cache[i] = (i < cnt) ? s[beg + i] : 0u;
+    for (int i = 0; i < PTC; i += 4) {
+      if (vec_ok && i + 4 <= cnt) {
+        const u32x4 v = ld16(s + beg + i);
+        cache[i] = v[0]; cache[i + 1] = v[1]; cache[i + 2] = v[2]; cache[i + 3] = v[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cache[i + e] = (i + e < cnt) ? s[beg + i + e] : 0u;
+      }
+    }
   }
   auto val = [&](int i) -> uint32_t {
     if constexpr (PTC > 0) return cache[i];
@@ -98,12 +123,12 @@ select_kernel(const SelectArgs args) {
 #pragma unroll
       for (int i = 0; i < PTC; ++i) {
         const uint32_t u = cache[i];
-        if (i < cnt && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        hist_add(hist, i < cnt && (u & pmask) == prefix, (u >> shift) & 255u);
       }
     } else {
-      for (int i = 0; i < cnt; ++i) {
-        const uint32_t u = val(i);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+      for (int i = 0; i < per; ++i) {  // same trip count in every lane (wave votes)
+        const uint32_t u = i < cnt ? val(i) : 0u;
+        hist_add(hist, i < cnt && (u & pmask) == prefix, (u >> shift) & 255u);
       }
     }
     __syncthreads();

@@ -117,7 +117,9 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
     q.c = (float)q.n - (float)(b ? b[i] : 1) - 0.5f;
     q.q0 = a ? first_live_row(q.n, a[i], b[i]) : 0;
     q.pr = G * (q.n - q.q0);
-    q.fr = fr_ok && q.n > 0 && q.pr <= FR_ROWS;
+    // few-rows kernels address a sequence's K span with 32-bit buffer offsets
+    const bool span_ok = (int64_t)q.n * s->kv_stride_tok * elt_bytes(s->dtype) < (int64_t(1) << 31);
+    q.fr = fr_ok && span_ok && q.n > 0 && q.pr <= FR_ROWS;
     q.rg = q.fr ? 0 : (q.pr + WGROWS1 - 1) / WGROWS1;
     q.nc = 1;
     q.kc = std::max(32, round32(q.n));
