@@ -189,25 +189,54 @@ few_rows_kernel(const FrArgs args) {
     lsum[t] = 0.f;
   }
 
-  // Pass-1 state update from 16 exponentials of one row tile; moves the
-  // reference (rescaling the sum) when the sum overflows past 2^64, is NaN,
-  // or the lane has no reference yet.  x: the 16 logits (masked ones -inf).
-  auto p1_update = [&](int t, const float* x, const float* pv) {
-    const float ln = lsum[t] + sum16(pv);
-    if (ln < 0x1p64f) {
-      lsum[t] = ln;
+  // Pass-1 logits of row tile t in sub-tile ktj (acc holds dot products):
+  // on a sub-tile crossing the diagonal, keys past the lane's row are -inf.
+  auto p1_logits = [&](const f32x16& a, int t, bool diag, int ktj, float* x) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      x[v] = (diag && ktj + out_row(v, hf) > qrow[t]) ? -INFINITY : a[v];
+  };
+  // Pass-1 reference move for row tile t: taken when the tile would carry
+  // the lane's sum past 2^64, makes it NaN, or the lane has no reference yet
+  // (its exponentials are then +inf or NaN); the sum is rescaled to the new
+  // reference.  Rare, so it is checked once per sub-tile, after every tile's
+  // exponentials: all of them then share one basic block with the next
+  // sub-tile's MFMAs.
+  auto p1_rescale = [&](int t, const float* x) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
+    if (mx != -INFINITY) {
+      const float mnew = fmaxf(mref[t], mx * cl2);
+      float p2[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p2[v] = fast_exp2(fmaf(x[v], cl2, -mnew));
+      const float alpha = (mref[t] == -INFINITY) ? 0.f : fast_exp2(mref[t] - mnew);
+      lsum[t] = lsum[t] * alpha + sum16(p2);
+      mref[t] = mnew;
+    }
+  };
+  // ln[t]: candidate sums; tiles with ln[t] < 2^64 take them, others move
+  // their reference.  diag/ktj as for p1_logits; live[t] false: tile skipped.
+  auto p1_commit = [&](const f32x16* acc, const float* ln, const bool* live, bool diag, int ktj) {
+    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < FR_TW; ++t) ok = ok && (!live[t] || ln[t] < 0x1p64f);
+    if (__builtin_expect(ok, 1)) {
+#pragma unroll
+      for (int t = 0; t < FR_TW; ++t)
+        if (live[t]) lsum[t] = ln[t];
     } else {
-      float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
-      if (mx != -INFINITY) {
-        const float mnew = fmaxf(mref[t], mx * cl2);
-        float p2[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) p2[v] = fast_exp2(fmaf(x[v], cl2, -mnew));
-        const float alpha = (mref[t] == -INFINITY) ? 0.f : fast_exp2(mref[t] - mnew);
-        lsum[t] = lsum[t] * alpha + sum16(p2);
-        mref[t] = mnew;
+      for (int t = 0; t < FR_TW; ++t) {
+        if (!live[t]) continue;
+        if (ln[t] < 0x1p64f) {
+          lsum[t] = ln[t];
+        } else {
+          float x[16];
+          p1_logits(acc[t], t, diag, ktj, x);
+          p1_rescale(t, x);
+        }
       }
     }
   };
@@ -215,6 +244,8 @@ few_rows_kernel(const FrArgs args) {
   // Epilogue of a sub-tile strictly below the causal diagonal of every row of
   // this workgroup (no masks, no branches before the sums).
   auto epi_clean = [&](f32x16* acc, float& csum) {
+    float ln[FR_TW];
+    bool live[FR_TW];
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
       float pv[16];
@@ -225,12 +256,11 @@ few_rows_kernel(const FrArgs args) {
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(acc[t][v], cl2, -mref[t]));
-        float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = acc[t][v];
-        p1_update(t, x, pv);
+        ln[t] = lsum[t] + sum16(pv);
+        live[t] = true;
       }
     }
+    if constexpr (!PASS2) p1_commit(acc, ln, live, false, 0);
   };
 
   // Epilogue of any other sub-tile: chunk padding (skipped), sub-tiles no row
@@ -238,10 +268,16 @@ few_rows_kernel(const FrArgs args) {
   auto epi_general = [&](f32x16* acc, int j, float& csum) {
     if (j < 0 || j >= nsub) return;
     const int ktj = kbeg + j * TILE;
+    float ln[FR_TW];
+    bool live[FR_TW];
+    bool diag_any = false;
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
-      if (!tval[t] || ktj > thi[t]) continue;
+      live[t] = tval[t] && ktj <= thi[t];
+      ln[t] = lsum[t];
+      if (!live[t]) continue;
       const bool diag = ktj + TILE - 1 > tlo[t];
+      diag_any = diag_any || diag;
       float pv[16];
       if constexpr (PASS2) {
 #pragma unroll
@@ -260,18 +296,15 @@ few_rows_kernel(const FrArgs args) {
         csum += sum16(pv);
       } else {
         float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = acc[t][v];
-        if (diag) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (ktj + out_row(v, hf) > qrow[t]) x[v] = -INFINITY;
-        }
+        p1_logits(acc[t], t, diag, ktj, x);
 #pragma unroll
         for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(x[v], cl2, -mref[t]));
-        p1_update(t, x, pv);
+        ln[t] = lsum[t] + sum16(pv);
       }
     }
+    // masking a tile that does not cross the diagonal changes nothing, so
+    // the rare path may mask every tile when any one crosses it
+    if constexpr (!PASS2) p1_commit(acc, ln, live, diag_any, ktj);
   };
 
   auto read_k = [&](int buf, int u, u32x4* kf) {
