@@ -12,4 +12,5 @@ from .waits import (  # noqa: F401
     score,
     score_select_compact,
     select,
+    select_compact,
 )

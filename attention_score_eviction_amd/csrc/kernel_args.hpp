@@ -71,6 +71,15 @@ struct SelectArgs {
   int64_t T;
   int32_t hkv;
   int32_t budget;
+  // Gather fused into the select launch (select_kernel<..., true> only):
+  // rows of K and V at the kept positions, zero rows past the kept count.
+  const unsigned char* k;
+  const unsigned char* v;
+  unsigned char* k_out;       // [nb, Hkv, budget, d] (this launch's slice)
+  unsigned char* v_out;
+  Strides st;                 // kv_* used
+  int32_t elt;                // bytes per element
+  int32_t row_shift;          // log2 of the 16-byte vectors per row
   SeqTable tab;
 };
 

@@ -4,13 +4,32 @@
 //
 // select_kernel: one 1024-thread workgroup per (sequence, KV head).  Scores
 // are non-negative fp32, so their bit patterns order like the values; an
-// MSB-first radix select (4 digits of 8 bits, LDS histograms) finds the bit
-// pattern T of the budget-th largest score and how many of the kept keys
-// must equal T.  An ordered pass then keeps every key above T plus the
-// lowest-positioned keys equal to T (ties go to the lower position), writing
-// positions in ascending order.  Each thread owns a contiguous run of
-// positions; runs of up to PTC scores stay in registers across the passes,
-// longer runs are re-read (from L2) on every pass.
+// MSB-first radix select (4 digits of 8 bits) finds the bit pattern T of the
+// budget-th largest score and how many of the kept keys must equal T.  Keys
+// above T, then the lowest-positioned keys equal to T (ties go to the lower
+// position), are written in ascending position order.
+//
+// Layout: wave w owns the contiguous key segment [w * seg, (w + 1) * seg)
+// (seg a multiple of 64), lane l its keys w * seg + 64 i + l, so every load
+// is coalesced and position order is (wave, i, lane) order.  Segments of up
+// to 64 * PTC keys stay in registers across the passes; longer ones are
+// re-read (from L2) on every pass.
+//
+// Histograms: the first digit is shared by almost every key, so its counts
+// go to per-(digit, lane % 32) words (the lanes of one atomic hit distinct
+// words instead of serialising on one) and are then folded into 256 digit
+// counts; later passes see few matching keys and count directly.  Every wave
+// derives the picked digit from the histogram itself: one barrier per pass
+// (two for the first).
+//
+// Output: a key's slot is (#kept keys above T before it) + min(#keys equal
+// to T before it, the number of T-equal keys kept), from wave ballots, their
+// prefix within the wave and a prefix over the 16 wave totals; no block
+// scan, no atomics.
+//
+// FUSE: the same workgroup then gathers the kept K and V rows (bit copies,
+// 16-byte vectors; zero rows past the kept count), so select and compact are
+// one launch.
 //
 // compact_kernel: one 16-byte vector per thread, rows of K and V copied bit
 // for bit; empty slots (-1) are zero-filled.
@@ -23,57 +42,46 @@ namespace waits {
 
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
+constexpr int SEL_SUB = 32;          // sub-counters per digit
+constexpr int SEL_FUSE_MAX = 8192;   // largest budget the fused gather keeps in LDS
 
-// Exclusive prefix sum over the workgroup in thread order; returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Wave-uniform pick from a 256-bin histogram: the digit d whose keys hold the
+// krem-th largest (counting from the highest digit), and how many keys lie
+// in higher digits.  Every wave computes it, so no barrier hands it out.
+__device__ __forceinline__ void pick_digit(const int* hist, int krem, int lane, int& digit,
+                                           int& above_out) {
+  // lane L holds digits 255-4L .. 252-4L (highest digits first)
+  int hv[4], lsum = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
+  for (int j = 0; j < 4; ++j) {
+    hv[j] = hist[255 - 4 * lane - j];
+    lsum += hv[j];
   }
-  if (lane == 63) sh[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    const int x = lane < SEL_WAVES ? sh[lane] : 0;
-    int xi = x;
+  int above = wave_incl_scan(lsum) - lsum, myd = -1, mya = 0;
 #pragma unroll
-    for (int d = 1; d < SEL_WAVES; d <<= 1) {
-      const int y = __shfl_up(xi, d, 64);
-      if (lane >= d) xi += y;
+  for (int j = 0; j < 4; ++j) {
+    if (above < krem && krem <= above + hv[j]) {
+      myd = 255 - 4 * lane - j;
+      mya = above;
     }
-    if (lane < SEL_WAVES) sh[lane] = xi - x;
-    if (lane == SEL_WAVES - 1) sh[SEL_WAVES] = xi;
+    above += hv[j];
   }
-  __syncthreads();
-  const int out = incl - v + sh[wave];
-  total = sh[SEL_WAVES];
-  __syncthreads();
-  return out;
+  const int src = __builtin_ctzll(__ballot(myd >= 0));  // exactly one lane
+  digit = __builtin_amdgcn_readlane(myd, src);
+  above_out = __builtin_amdgcn_readlane(mya, src);
 }
 
-// hist[d] += 1 for every active lane whose value matches; lanes that agree
-// with the wave's first candidate digit are counted with one atomic (the
-// leading radix digits of similar-magnitude scores are shared by almost all
-// keys, so per-lane atomics would serialise on one LDS word).
-__device__ __forceinline__ void hist_add(int* hist, bool take, uint32_t d) {
-  const uint64_t cand = __ballot(take);
-  if (cand == 0) return;
-  const int leader = __builtin_ctzll(cand);
-  const uint32_t ld = __shfl(d, leader, 64);
-  const uint64_t same = __ballot(take && d == ld);
-  const int lane = threadIdx.x & 63;
-  if (lane == leader) atomicAdd(&hist[ld], __builtin_popcountll(same));
-  else if (take && d != ld) atomicAdd(&hist[d], 1);
-}
-
-template <int PTC>
+template <int PTC, bool FUSE>
 __global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs args) {
-  __shared__ int hist[256];
-  __shared__ int scan_sh[SEL_WAVES + 1];
-  __shared__ int pick[2];
+  __shared__ __attribute__((aligned(16))) int sub[256 * SEL_SUB];
+  __shared__ int hist[4][256];
+  __shared__ int wtot[2][SEL_WAVES];
+  __shared__ int sel[FUSE ? SEL_FUSE_MAX : 1];
 
   const SeqTable& tab = args.tab;
   const int item = blockIdx.x;
@@ -83,123 +91,145 @@ select_kernel(const SelectArgs args) {
   const int budget = args.budget;
   const int keep = min(budget, N);
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int32_t* out = args.idx + ((int64_t)p * args.hkv + h) * budget;
   for (int j = keep + tid; j < budget; j += SEL_THREADS) out[j] = -1;
+
   if (keep == N) {  // every key is kept
-    for (int j = tid; j < N; j += SEL_THREADS) out[j] = j;
-    return;
-  }
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)h * args.T + tab.tok0[p]);
-
-  const int per = ((N + SEL_THREADS - 1) / SEL_THREADS + 3) & ~3;  // multiple of 4
-  const int beg = min(tid * per, N);
-  const int cnt = min(per, N - beg);
-  uint32_t cache[PTC > 0 ? PTC : 1];
-  // runs start at multiples of 4 scores: 16-byte aligned when the head's row is
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;
-  if constexpr (PTC > 0) {
-#pragma unroll
-    for (int i = 0; i < PTC; i += 4) {
-      if (vec_ok && i + 4 <= cnt) {
-        const u32x4 v = ld16(s + beg + i);
-        cache[i] = v[0]; cache[i + 1] = v[1]; cache[i + 2] = v[2]; cache[i + 3] = v[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cache[i + e] = (i + e < cnt) ? s[beg + i + e] : 0u;
-      }
+    for (int j = tid; j < N; j += SEL_THREADS) {
+      out[j] = j;
+      if constexpr (FUSE) sel[j] = j;
     }
-  }
-  auto val = [&](int i) -> uint32_t {
-    if constexpr (PTC > 0) return cache[i];
-    else return s[beg + i];
-  };
-
-  uint32_t prefix = 0, pmask = 0;
-  int krem = keep;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  } else {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)h * args.T + tab.tok0[p]);
+    const int seg = (N + SEL_THREADS - 1) / SEL_THREADS * WAVE;  // keys per wave, multiple of 64
+    const int iters = seg / WAVE;
+    const int e0 = wave * seg + lane;
+    uint32_t cache[PTC > 0 ? PTC : 1];
     if constexpr (PTC > 0) {
 #pragma unroll
       for (int i = 0; i < PTC; ++i) {
-        const uint32_t u = cache[i];
-        hist_add(hist, i < cnt && (u & pmask) == prefix, (u >> shift) & 255u);
-      }
-    } else {
-      for (int i = 0; i < per; ++i) {  // same trip count in every lane (wave votes)
-        const uint32_t u = i < cnt ? val(i) : 0u;
-        hist_add(hist, i < cnt && (u & pmask) == prefix, (u >> shift) & 255u);
+        const int e = e0 + i * WAVE;
+        cache[i] = (i < iters && e < N) ? s[e] : 0u;
       }
     }
+    for (int i = tid; i < 256 * SEL_SUB / 4; i += SEL_THREADS)
+      reinterpret_cast<int4*>(sub)[i] = int4{0, 0, 0, 0};
+    hist[tid >> 8][tid & 255] = 0;
+    static_assert(SEL_THREADS == 4 * 256, "one histogram word per thread");
     __syncthreads();
-    if (tid < 64) {
-      // lane L holds digits 255-4L .. 252-4L (highest digits first)
-      int hv[4], lsum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hv[j] = hist[255 - 4 * tid - j];
-        lsum += hv[j];
-      }
-      int incl = lsum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (tid >= d) incl += y;
-      }
-      int above = incl - lsum;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (above < krem && krem <= above + hv[j]) {
-          pick[0] = 255 - 4 * tid - j;
-          pick[1] = above;
-        }
-        above += hv[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t dgt = (uint32_t)pick[0];
-    krem -= pick[1];
-    prefix |= dgt << shift;
-    pmask |= 255u << shift;
-  }
-  const uint32_t thr = prefix;
-  const int need_eq = krem;  // keys equal to thr that are kept (lowest positions)
 
-  int n_gt = 0, n_eq = 0;
-  if constexpr (PTC > 0) {
+    // f(i, valid, bits) over this lane's keys, in position order; with a
+    // register cache, `live` (bit i: some lane of the wave still matches the
+    // prefix with its i-th key) skips keys no lane needs.
+    uint32_t live = ~0u;
+    auto each_key = [&](auto&& f) {
+      if constexpr (PTC > 0) {
 #pragma unroll
-    for (int i = 0; i < PTC; ++i) {
-      if (i < cnt) {
-        n_gt += cache[i] > thr;
-        n_eq += cache[i] == thr;
+        for (int i = 0; i < PTC; ++i)
+          if (i < iters && ((live >> i) & 1u)) f(i, e0 + i * WAVE < N, cache[i]);  // wave-uniform
+      } else {
+        for (int i = 0; i < iters; ++i) {
+          const int e = e0 + i * WAVE;
+          f(i, e < N, e < N ? s[e] : 0u);
+        }
       }
+    };
+
+    // pass 1 (top digit, shared by almost every key): per-(digit, lane % 32)
+    // counters keep the lanes of one atomic on distinct words
+    {
+      int* mysub = sub + (lane & (SEL_SUB - 1));
+      each_key([&](int, bool ok, uint32_t u) {
+        if (ok) atomicAdd(mysub + (u >> 24) * SEL_SUB, 1);
+      });
+      __syncthreads();
+      const int d = tid >> 2, part = tid & 3;
+      const int4* q4 = reinterpret_cast<const int4*>(sub + d * SEL_SUB + part * 8);
+      const int4 x = q4[0], y = q4[1];
+      const int c = quad_sum((x.x + x.y) + (x.z + x.w) + (y.x + y.y) + (y.z + y.w));
+      if (part == 0) hist[0][d] = c;
+      __syncthreads();
     }
-  } else {
-    for (int i = 0; i < cnt; ++i) {
-      const uint32_t u = val(i);
-      n_gt += u > thr;
-      n_eq += u == thr;
-    }
-  }
-  int tot;
-  const int gt_before = block_exclusive_scan(n_gt, scan_sh, tot);
-  const int eq_before = block_exclusive_scan(n_eq, scan_sh, tot);
-  int pos = gt_before + min(eq_before, need_eq);
-  int eq_rank = eq_before;
-  auto emit = [&](int i, uint32_t u) {
-    if (u > thr) {
-      out[pos++] = beg + i;
-    } else if (u == thr) {
-      if (eq_rank < need_eq) out[pos++] = beg + i;
-      ++eq_rank;
-    }
-  };
-  if constexpr (PTC > 0) {
+    int dgt, above;
+    pick_digit(hist[0], keep, lane, dgt, above);
+    uint32_t prefix = (uint32_t)dgt << 24, pmask = 0xFF000000u;
+    int krem = keep - above;
+
+    // passes 2-4: few keys still match, so plain atomics on one histogram
+    // per pass (cleared at the start: no clearing between passes)
 #pragma unroll
-    for (int i = 0; i < PTC; ++i)
-      if (i < cnt) emit(i, cache[i]);
-  } else {
-    for (int i = 0; i < cnt; ++i) emit(i, val(i));
+    for (int pass = 1; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t nlive = 0;
+      each_key([&](int i, bool ok, uint32_t u) {
+        const bool take = ok && (u & pmask) == prefix;
+        const uint64_t m = __ballot(take);
+        nlive |= (m != 0 ? 1u : 0u) << i;
+        if (take) atomicAdd(&hist[pass][(u >> shift) & 255u], 1);
+      });
+      if constexpr (PTC > 0) live = nlive;
+      __syncthreads();
+      pick_digit(hist[pass], krem, lane, dgt, above);
+      krem -= above;
+      prefix |= (uint32_t)dgt << shift;
+      pmask |= 255u << shift;
+    }
+    const uint32_t thr = prefix;
+    const int need_eq = krem;  // keys equal to thr that are kept (lowest positions)
+    live = ~0u;
+
+    int n_gt = 0, n_eq = 0;  // wave totals (uniform)
+    each_key([&](int, bool ok, uint32_t u) {
+      n_gt += __builtin_popcountll(__ballot(ok && u > thr));
+      n_eq += __builtin_popcountll(__ballot(ok && u == thr));
+    });
+    if (lane == 0) {
+      wtot[0][wave] = n_gt;
+      wtot[1][wave] = n_eq;
+    }
+    __syncthreads();
+    // keys above / equal to thr in earlier waves
+    int gb = wave_incl_scan(lane < wave ? wtot[0][lane] : 0);
+    int eb = wave_incl_scan(lane < wave ? wtot[1][lane] : 0);
+    gb = __builtin_amdgcn_readlane(gb, SEL_WAVES - 1);
+    eb = __builtin_amdgcn_readlane(eb, SEL_WAVES - 1);
+    each_key([&](int i, bool ok, uint32_t u) {
+      const bool gt = ok && u > thr, eq = ok && u == thr;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      if ((mg | me) == 0) return;  // wave-uniform
+      const int g_before = gb + lanes_below(mg);
+      const int e_before = eb + lanes_below(me);
+      if (gt || (eq && e_before < need_eq)) {
+        const int slot = g_before + min(e_before, need_eq);
+        const int e = e0 + i * WAVE;
+        out[slot] = e;
+        if constexpr (FUSE) sel[slot] = e;
+      }
+      gb += __builtin_popcountll(mg);
+      eb += __builtin_popcountll(me);
+    });
+  }
+
+  if constexpr (FUSE) {
+    __syncthreads();
+    const int vs = args.row_shift;
+    const int rb = 16 << vs;  // row bytes
+    const int total = budget << vs;
+    const int64_t obase = ((int64_t)p * args.hkv + h) * budget * rb;
+    const int64_t kbase = ((int64_t)tab.tok0[p] * args.st.kv_tok + (int64_t)h * args.st.kv_head) * args.elt;
+    for (int x = tid; x < total; x += SEL_THREADS) {
+      const int j = x >> vs, c = x & ((1 << vs) - 1);
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (j < keep) {
+        const int64_t src = kbase + (int64_t)sel[j] * args.st.kv_tok * args.elt + c * 16;
+        kv = ld16(args.k + src);
+        vv = ld16(args.v + src);
+      }
+      st16(args.k_out + obase + (int64_t)j * rb + c * 16, kv);
+      st16(args.v_out + obase + (int64_t)j * rb + c * 16, vv);
+    }
   }
 }
 

@@ -377,6 +377,93 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
   return WAITS_OK;
 }
 
+int check_select(const waits_shape* s, const float* scores, int32_t budget, const int32_t* idx) {
+  if (!s || !s->cu_seqlens || s->batch < 1 || s->n_kv_heads < 1 || s->cu_seqlens[0] != 0)
+    return WAITS_EINVAL;
+  for (int i = 0; i < s->batch; ++i) {
+    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
+  }
+  if (budget < 1 || !idx || !is_aligned(idx, 4)) return WAITS_EINVAL;
+  if (s->cu_seqlens[s->batch] > 0 && (!scores || !is_aligned(scores, 4))) return WAITS_EINVAL;
+  return WAITS_OK;
+}
+
+int check_gather(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
+                 int32_t budget, const void* k_out, const void* v_out) {
+  if (budget < 1 || !idx || !k_out || !v_out || !is_aligned(idx, 4) || !is_aligned(k_out, 16) ||
+      !is_aligned(v_out, 16))
+    return WAITS_EINVAL;
+  if (s->cu_seqlens[s->batch] > 0 && (!k || !v || !is_aligned(k, 16) || !is_aligned(v, 16)))
+    return WAITS_EINVAL;
+  return WAITS_OK;
+}
+
+template <bool FUSE>
+int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
+               const void* k, const void* vv, void* k_out, void* v_out, hipStream_t stream) {
+  const std::vector<Seq> v = plan_seqs(s, nullptr, nullptr);
+  const int e = FUSE ? elt_bytes(s->dtype) : 0;
+  const int row_bytes = FUSE ? s->head_dim * e : 0;
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
+    SelectArgs args;
+    args.scores = scores;
+    args.idx = idx + first_row;
+    args.T = s->cu_seqlens[s->batch];
+    args.hkv = s->n_kv_heads;
+    args.budget = budget;
+    args.k = static_cast<const unsigned char*>(k);
+    args.v = static_cast<const unsigned char*>(vv);
+    args.k_out = FUSE ? static_cast<unsigned char*>(k_out) + first_row * row_bytes : nullptr;
+    args.v_out = FUSE ? static_cast<unsigned char*>(v_out) + first_row * row_bytes : nullptr;
+    args.st = strides_of(s);
+    args.elt = e;
+    args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
+    fill_table(args.tab, v, lo, hi, s->n_kv_heads);
+    int gmax = 0;
+    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+    const dim3 grid((hi - lo) * s->n_kv_heads);
+    if (gmax <= SEL_THREADS * 16)
+      hipLaunchKernelGGL((select_kernel<16, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+    else if (gmax <= SEL_THREADS * 32)
+      hipLaunchKernelGGL((select_kernel<32, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+    else
+      hipLaunchKernelGGL((select_kernel<0, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
+int run_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
+                int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
+  const std::vector<Seq> sq = plan_seqs(s, nullptr, nullptr);
+  const int e = elt_bytes(s->dtype);
+  const int row_bytes = s->head_dim * e;
+  const int rows_per_block = 256 / (row_bytes / 16);
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
+    CompactArgs args;
+    args.k = static_cast<const unsigned char*>(k);
+    args.v = static_cast<const unsigned char*>(v);
+    args.idx = idx + first_row;
+    args.k_out = static_cast<unsigned char*>(k_out) + first_row * row_bytes;
+    args.v_out = static_cast<unsigned char*>(v_out) + first_row * row_bytes;
+    args.st = strides_of(s);
+    args.rows = (int64_t)(hi - lo) * s->n_kv_heads * budget;
+    args.hkv = s->n_kv_heads;
+    args.budget = budget;
+    args.elt = e;
+    fill_table(args.tab, sq, lo, hi, s->n_kv_heads);
+    const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
 }  // namespace
 }  // namespace waits
 
@@ -461,74 +548,32 @@ int waits_score(const waits_shape* s, const void* q, const void* k, const float*
 
 int waits_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
                  hipStream_t stream) {
-  if (!s || !s->cu_seqlens || s->batch < 1 || s->n_kv_heads < 1 || s->cu_seqlens[0] != 0)
-    return WAITS_EINVAL;
-  int maxn = 0;
-  for (int i = 0; i < s->batch; ++i) {
-    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
-    if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
-    maxn = std::max(maxn, (int)n);
-  }
-  if (budget < 1 || !idx || !is_aligned(idx, 4)) return WAITS_EINVAL;
-  if (s->cu_seqlens[s->batch] > 0 && (!scores || !is_aligned(scores, 4))) return WAITS_EINVAL;
-  const std::vector<Seq> v = plan_seqs(s, nullptr, nullptr);
-  for (int lo = 0; lo < s->batch; lo += MAXB) {
-    const int hi = std::min(s->batch, lo + MAXB);
-    SelectArgs args;
-    args.scores = scores;
-    args.idx = idx + (int64_t)lo * s->n_kv_heads * budget;
-    args.T = s->cu_seqlens[s->batch];
-    args.hkv = s->n_kv_heads;
-    args.budget = budget;
-    fill_table(args.tab, v, lo, hi, s->n_kv_heads);
-    int gmax = 0;
-    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
-    const dim3 grid((hi - lo) * s->n_kv_heads);
-    if (gmax <= SEL_THREADS * 16)
-      hipLaunchKernelGGL(select_kernel<16>, grid, dim3(SEL_THREADS), 0, stream, args);
-    else if (gmax <= SEL_THREADS * 32)
-      hipLaunchKernelGGL(select_kernel<32>, grid, dim3(SEL_THREADS), 0, stream, args);
-    else
-      hipLaunchKernelGGL(select_kernel<0>, grid, dim3(SEL_THREADS), 0, stream, args);
-    if (launched() != WAITS_OK) return WAITS_EDEVICE;
-  }
-  (void)maxn;
-  return WAITS_OK;
+  const int rc = check_select(s, scores, budget, idx);
+  if (rc != WAITS_OK) return rc;
+  return run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 int waits_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
                   int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
-  const int rc = check_shape(s, false);
+  int rc = check_shape(s, false);
+  if (rc == WAITS_OK) rc = check_gather(s, k, v, idx, budget, k_out, v_out);
   if (rc != WAITS_OK) return rc;
-  if (budget < 1 || !idx || !k_out || !v_out || !is_aligned(idx, 4) || !is_aligned(k_out, 16) ||
-      !is_aligned(v_out, 16))
-    return WAITS_EINVAL;
-  if (s->cu_seqlens[s->batch] > 0 && (!k || !v || !is_aligned(k, 16) || !is_aligned(v, 16)))
-    return WAITS_EINVAL;
-  const std::vector<Seq> sq = plan_seqs(s, nullptr, nullptr);
-  const int e = elt_bytes(s->dtype);
-  const int row_bytes = s->head_dim * e;
-  const int rows_per_block = 256 / (row_bytes / 16);
-  for (int lo = 0; lo < s->batch; lo += MAXB) {
-    const int hi = std::min(s->batch, lo + MAXB);
-    const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
-    CompactArgs args;
-    args.k = static_cast<const unsigned char*>(k);
-    args.v = static_cast<const unsigned char*>(v);
-    args.idx = idx + first_row;
-    args.k_out = static_cast<unsigned char*>(k_out) + first_row * row_bytes;
-    args.v_out = static_cast<unsigned char*>(v_out) + first_row * row_bytes;
-    args.st = strides_of(s);
-    args.rows = (int64_t)(hi - lo) * s->n_kv_heads * budget;
-    args.hkv = s->n_kv_heads;
-    args.budget = budget;
-    args.elt = e;
-    fill_table(args.tab, sq, lo, hi, s->n_kv_heads);
-    const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
-    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  return run_compact(s, k, v, idx, budget, k_out, v_out, stream);
+}
+
+int waits_select_compact(const waits_shape* s, const float* scores, const void* k, const void* v,
+                         int32_t budget, int32_t* idx, void* k_out, void* v_out,
+                         hipStream_t stream) {
+  int rc = check_shape(s, false);
+  if (rc == WAITS_OK) rc = check_select(s, scores, budget, idx);
+  if (rc == WAITS_OK) rc = check_gather(s, k, v, idx, budget, k_out, v_out);
+  if (rc != WAITS_OK) return rc;
+  if (budget > SEL_FUSE_MAX) {
+    rc = run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, stream);
+    if (rc != WAITS_OK) return rc;
+    return run_compact(s, k, v, idx, budget, k_out, v_out, stream);
   }
-  return WAITS_OK;
+  return run_select<true>(s, scores, budget, idx, k, v, k_out, v_out, stream);
 }
 
 const char* waits_strerror(int code) {

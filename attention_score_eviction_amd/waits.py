@@ -65,6 +65,7 @@ _SIGS = {
     "waits_score": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
     "waits_select": [_SP, _P, ctypes.c_int32, _P, _P],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
+    "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P],
 }
 
 
@@ -286,9 +287,31 @@ def compact(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, cu_seqlens, bud
     return k_out, v_out
 
 
+def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
+                   budget: int, idx: Optional[torch.Tensor] = None,
+                   k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None):
+    """select() then compact() in one launch: (idx, k_out, v_out)."""
+    _last_dim_contiguous(k, v)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    m = _Marshal(cu_seqlens, None, k, 1.0)
+    nb, hkv, d = len(m.cu) - 1, k.shape[1], k.shape[2]
+    if scores.shape[0] != hkv:
+        raise ValueError("scores must be [n_kv_heads, T]")
+    if idx is None:
+        idx = torch.empty((nb, hkv, int(budget)), dtype=torch.int32, device=k.device)
+    if k_out is None:
+        k_out = torch.empty((nb, hkv, int(budget), d), dtype=k.dtype, device=k.device)
+    if v_out is None:
+        v_out = torch.empty((nb, hkv, int(budget), d), dtype=v.dtype, device=v.device)
+    _check("waits_select_compact", lib().waits_select_compact(
+        m.sp, _ptr(scores), _ptr(k), _ptr(v), int(budget), _ptr(idx), _ptr(k_out), _ptr(v_out),
+        _stream(k)))
+    return idx, k_out, v_out
+
+
 def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None):
     """The whole path: scores, kept positions and the compacted K/V."""
     s = score(q, k, cu_seqlens, a, b, scale)
-    idx = select(s, cu_seqlens, budget)
-    kc, vc = compact(k, v, idx, cu_seqlens, budget)
+    idx, kc, vc = select_compact(s, k, v, cu_seqlens, budget)
     return s, idx, kc, vc

@@ -241,7 +241,7 @@ def main():
     vc = torch.empty_like(kc)
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
     def step(e=None):
         if e: e[0].record(stream)
@@ -249,10 +249,8 @@ def main():
         if e: e[1].record(stream)
         W.colsum(q, k, lse, cu, a, b, out=scores)
         if e: e[2].record(stream)
-        W.select(scores, cu, budget, out=idx)
+        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc)  # one launch
         if e: e[3].record(stream)
-        W.compact(k, v, idx, cu, budget, k_out=kc, v_out=vc)
-        if e: e[4].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -264,7 +262,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    names = ["pass1_lse", "pass2_colsum", "select", "compact"]
+    names = ["pass1_lse", "pass2_colsum", "select_compact"]
     per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            for j, nm in enumerate(names)}  # ms per launch (pass 1 includes its combine, if any)
 
@@ -275,13 +273,12 @@ def main():
     frac = {
         "pass1_lse": flops_pass / (per["pass1_lse"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "pass2_colsum": flops_pass / (per["pass2_colsum"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "select": sel_bytes / (per["select"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "compact": cmp_bytes / (per["compact"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "select_compact": (sel_bytes + cmp_bytes) / (per["select_compact"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     dom = max(("pass1_lse", "pass2_colsum"), key=lambda nm: per[nm])
     achieved = flops_pass / (per[dom] * 1e-3) / 1e12
     passes_ms = per["pass1_lse"] + per["pass2_colsum"]
-    sc_ms = per["select"] + per["compact"]
+    sc_ms = per["select_compact"]
 
     out = {
         "metric": METRIC,

@@ -156,6 +156,20 @@ int waits_compact(const waits_shape* shape, const void* k, const void* v,
                   const int32_t* idx, int32_t select_budget, void* k_out,
                   void* v_out, hipStream_t stream);
 
+/*
+ * Selection and compaction in one launch: the outputs of waits_select
+ * (idx) followed by waits_compact (k_out, v_out), with the same arguments,
+ * layouts and error codes as those two calls, bit for bit.  The workgroup
+ * that selects a (sequence, KV head) gathers its rows while the positions
+ * are still in LDS, so the gather needs no second launch and no re-read of
+ * idx.  For select_budget > 8192 it runs the two kernels one after the
+ * other on `stream`.
+ */
+int waits_select_compact(const waits_shape* shape, const float* scores,
+                         const void* k, const void* v, int32_t select_budget,
+                         int32_t* idx, void* k_out, void* v_out,
+                         hipStream_t stream);
+
 /* Static description of a WAITS_E* code. */
 const char* waits_strerror(int code);
 

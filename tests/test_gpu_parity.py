@@ -282,6 +282,39 @@ def test_select_on_arbitrary_scores(n, budget):
         np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
 
 
+@pytest.mark.parametrize("n", [1, 63, 64, 1023, 1024, 1025, 16384, 16385, 32768, 32769, 65600])
+def test_select_segment_boundaries(n):
+    # key counts around the per-wave segment sizes and the register-cache limits
+    _say(f"select boundaries n={n}")
+    rng = np.random.default_rng(1000 + n)
+    s = (rng.random((2, n)) ** 6).astype(np.float32)
+    s[1, rng.integers(0, n, max(1, n // 4))] = np.float32(0.25)
+    for budget in (1, 128, min(n, 3000)):
+        idx = W.select(torch.from_numpy(s).to(DEV), [0, n], budget).cpu().numpy()
+        for h in range(2):
+            np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
+
+
+@pytest.mark.parametrize("lengths,budget", [([3000, 17000, 40, 0, 33000], 256), ([5000, 9000], 10000),
+                                            ([700] * 40, 64), ([128, 127, 129], 128)])
+def test_select_compact_fused_matches_separate(lengths, budget):
+    # one launch (select + gather) against waits_select then waits_compact, bit for bit
+    _say(f"fused select+compact lengths={lengths[:5]} budget={budget}")
+    bt = make_batch(list(range(60, 60 + len(lengths))), lengths, 4, 2, 128, heavy=True, values=True)
+    _, k, v = to_device(bt)
+    rng = np.random.default_rng(7)
+    T = int(bt.cu_seqlens[-1])
+    s = torch.from_numpy((rng.random((2, T)) ** 4).astype(np.float32)).to(DEV)
+    idx1 = W.select(s, bt.cu_seqlens, budget)
+    kc1, vc1 = W.compact(k, v, idx1, bt.cu_seqlens, budget)
+    idx2, kc2, vc2 = W.select_compact(s, k, v, bt.cu_seqlens, budget)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    check_compact(kc2, vc2, bt.k_bits, bt.v_bits, idx2.cpu().numpy(), bt.cu_seqlens)
+
+
 def test_compact_with_padding_slots():
     _say("compact padding")
     bt = make_batch([51, 52], [10, 300], 4, 2, 128, heavy=True)
