@@ -1,9 +1,11 @@
 // Both QK^T passes for sequences whose processed rows are few: when the G
 // query heads of a KV head have at most FR_ROWS packed rows in total (large
 // a: only the last rows carry weight), one workgroup holds every row of the
-// head in registers and streams K past them exactly once.
+// head in registers and streams K past them exactly once.  Pass 1 also runs
+// here for heads with more rows, one block of FR_ROWS packed rows per
+// workgroup (the block's keys end at its last query).
 //
-// Work item = (sequence, KV head h, key chunk).  8 waves; wave w owns packed
+// Work item = (sequence, KV head h, row block, key chunk).  8 waves; wave w owns packed
 // row tiles w and w + 8 (32 rows each, MFMA operand fragments in
 // registers).  K moves in stages of FR_SUB 32-key sub-tiles: HBM -> registers
 // (FR_RING stages of loads in flight) -> LDS (double buffer, one barrier per
@@ -79,12 +81,27 @@ few_rows_kernel(const FrArgs args) {
   const int local = item - tab.first[p];
   const int hkv = args.hkv, G = args.G;
   const int h = local % hkv;
-  const int chunk = local / hkv;
+  const int rest = local / hkv;
+  const int nc = tab.nc[p];
+  const int rb = tab.nrb[p] - 1 - rest / nc;  // row block (larger key ranges first)
+  const int chunk = rest - (rest / nc) * nc;
   const int N = tab.n[p], q0 = tab.q0[p];
   const int PR = G * (N - q0);
   const int64_t tok0 = tab.tok0[p];
-  const int kbeg = chunk * tab.kc[p];
-  const int kend = min(kbeg + tab.kc[p], N);
+  const int rbase = rb * FR_ROWS;             // first packed row of the block
+  const int qb0 = q0 + rbase / G;             // its first query
+  // Keys: pass 2 (one row block) the sequence's keys in chunks of kc; pass 1
+  // the keys up to the block's last query, cut into nc chunks.
+  int kbeg, kend;
+  if constexpr (PASS2) {
+    kbeg = chunk * tab.kc[p];
+    kend = min(kbeg + tab.kc[p], N);
+  } else {
+    const int nkeys = min(N, q0 + (min(rbase + FR_ROWS, PR) - 1) / G + 1);
+    const int kc = ((nkeys + nc - 1) / nc + TILE - 1) / TILE * TILE;
+    kbeg = chunk * kc;
+    kend = min(kbeg + kc, nkeys);
+  }
   const int nsub = (kend - kbeg + TILE - 1) / TILE;     // 32-key sub-tiles
   const int nst = (nsub + FR_SUB - 1) / FR_SUB;          // stages
 
@@ -95,15 +112,24 @@ few_rows_kernel(const FrArgs args) {
   const unsigned char* kb = static_cast<const unsigned char*>(args.k);
   const float cl2 = args.scale_log2;
 
+  if constexpr (!PASS2) {
+    if (kbeg >= kend) {  // a chunk past the block's keys: its partials are empty
+      for (int r = tid; r < FR_ROWS && rbase + r < PR; r += FR_THREADS)
+        args.part[tab.ws0[p] + ((int64_t)h * tab.prow[p] + rbase + r) * nc + chunk] =
+            make_float2(-INFINITY, 0.f);
+      return;
+    }
+  }
+
   // Row table (and pass-2 exponent offsets): one thread per packed row.
   for (int r = tid; r < FR_ROWS; r += FR_THREADS) {
     int q = -1;
     float off = INFINITY;
-    if (r < PR) {
-      const int j = r / G;
+    if (rbase + r < PR) {
+      const int j = (rbase + r) / G;
       q = q0 + j;
       if constexpr (PASS2) {
-        const int g = h * G + (r - j * G);
+        const int g = h * G + (rbase + r - j * G);
         const float lse = args.lse[(int64_t)g * args.T + tok0 + q];
         const float e = expf(-tab.a[p] * ((float)q - tab.c[p]));  // w = 1 / (1 + e)
         off = fmaf(lse, LOG2E, log2f(1.f + e));
@@ -120,7 +146,7 @@ few_rows_kernel(const FrArgs args) {
   int qrow[FR_TW];
 #pragma unroll
   for (int t = 0; t < FR_TW; ++t) {
-    const int r0 = (wave + t * FR_WAVES) * TILE;
+    const int r0 = rbase + (wave + t * FR_WAVES) * TILE;
     tval[t] = r0 < PR;
     tlo[t] = q0 + r0 / G;
     thi[t] = q0 + (min(r0 + TILE, PR) - 1) / G;
@@ -141,19 +167,21 @@ few_rows_kernel(const FrArgs args) {
   }
 
   // K staging: ring of FR_RING stages in registers, fetched with buffer loads
-  // over this sequence's rows of head h: one 32-bit offset add per load, and
-  // the hardware range check returns zeros past the sequence (the host sends
-  // a sequence here only when its K span fits 2^31 bytes).  Stages past the
-  // chunk re-read its last stage, so every thread issues the same number of
-  // loads per stage and the compiler waits for exactly the oldest stage.
-  // Rows past the chunk but inside the sequence carry real keys; they are
-  // never used: sub-tiles are 32-key aligned with the chunk end, sub-tiles
-  // past it skip their epilogue, and keys past the sequence are causal-masked
-  // (pass 1) or not written (pass 2).
+  // over head h's rows from the chunk's first key to the sequence end: one
+  // 32-bit offset add per load, and the hardware range check returns zeros
+  // past the sequence (the host keeps a chunk's K span below 2^31 bytes).
+  // Stages past the chunk re-read its last stage, so every thread issues the
+  // same number of loads per stage and the compiler waits for exactly the
+  // oldest stage.  Rows past the chunk but inside the sequence carry real
+  // keys; they are never used: sub-tiles are 32-key aligned with the chunk
+  // end, sub-tiles past it skip their epilogue, and keys past the sequence
+  // are causal-masked (pass 1) or not written (pass 2).
   const int row_bytes = (int)(args.st.kv_tok * Geo::ELT);
-  const unsigned char* kseq = kb + (tok0 * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT;
+  const unsigned char* kseq =
+      kb + ((tok0 + kbeg) * args.st.kv_tok + (int64_t)h * args.st.kv_head) * Geo::ELT;
+  const int krange = (int)min((int64_t)(N - kbeg) * row_bytes, (int64_t)0x7FFFFFFF);
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kseq), 0, N * row_bytes, BUFFER_RSRC_WORD3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kseq), 0, krange, BUFFER_RSRC_WORD3);
   int voff[SV];
 #pragma unroll
   for (int i = 0; i < SV; ++i) {
@@ -162,7 +190,7 @@ few_rows_kernel(const FrArgs args) {
   }
   u32x4 ring[FR_RING][SV];
   auto issue = [&](int stage, u32x4* dst) {
-    const int sbase = (kbeg + min(stage, nst - 1) * FR_STAGE) * row_bytes;
+    const int sbase = min(stage, nst - 1) * FR_STAGE * row_bytes;
 #pragma unroll
     for (int i = 0; i < SV; ++i)
       dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i] + sbase, 0, 0));
@@ -283,10 +311,10 @@ few_rows_kernel(const FrArgs args) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(fmaf(acc[t][v], cl2, -off[t][v]));
         if (diag) {
-          const int rbase = (wave + t * FR_WAVES) * TILE;
+          const int lrow = (wave + t * FR_WAVES) * TILE;  // tile's first row in the LDS tables
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int4 qv = *reinterpret_cast<const int4*>(&row_q[rbase + 8 * jj + 4 * hf]);
+            const int4 qv = *reinterpret_cast<const int4*>(&row_q[lrow + 8 * jj + 4 * hf]);
             const int qq[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -341,7 +369,7 @@ few_rows_kernel(const FrArgs args) {
   u32x4 kf[Geo::NV];
   auto subtile = [&](int buf, int u, int g) {
     const int j = g - 1;
-    const bool clean = j >= 0 && j < nsub && kbeg + j * TILE + TILE - 1 <= q0;
+    const bool clean = j >= 0 && j < nsub && kbeg + j * TILE + TILE - 1 <= qb0;
     float csum = 0.f;
     if (clean) {
       read_k(buf, u, kf);
@@ -367,10 +395,10 @@ few_rows_kernel(const FrArgs args) {
   if constexpr (PASS2) {
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
-      const int rbase = (wave + t * FR_WAVES) * TILE;
+      const int lrow = (wave + t * FR_WAVES) * TILE;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 ov = *reinterpret_cast<const f32x4*>(&row_off[rbase + 8 * jj + 4 * hf]);
+        const f32x4 ov = *reinterpret_cast<const f32x4*>(&row_off[lrow + 8 * jj + 4 * hf]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) off[t][4 * jj + e] = ov[e];
       }
@@ -415,7 +443,6 @@ few_rows_kernel(const FrArgs args) {
 #pragma unroll
     for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 1);
   } else {
-    const int nc = tab.nc[p];
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
       const float mo = wave_xor32(mref[t]);
@@ -427,13 +454,13 @@ few_rows_kernel(const FrArgs args) {
              (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - mx));
       }
       if (hf == 0 && qrow[t] >= 0) {
-        const int r = (wave + t * FR_WAVES) * TILE + col;
+        const int r = rbase + (wave + t * FR_WAVES) * TILE + col;
         const int j = r / G;
         const int g = h * G + (r - j * G);
         if (nc == 1) {
           args.lse[(int64_t)g * args.T + tok0 + qrow[t]] = (mx + log2f(lt)) * LN2;
         } else {
-          args.part[tab.ws0[p] + ((int64_t)h * FR_ROWS + r) * nc + chunk] = make_float2(mx, lt);
+          args.part[tab.ws0[p] + ((int64_t)h * tab.prow[p] + r) * nc + chunk] = make_float2(mx, lt);
         }
       }
     }

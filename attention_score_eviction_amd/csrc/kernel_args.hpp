@@ -14,9 +14,10 @@ struct SeqTable {
   int32_t n[MAXB];            // sequence length N
   int32_t q0[MAXB];           // first processed query row
   int32_t first[MAXB + 1];    // first work item of each sequence; first[nb] = total
-  int32_t rg[MAXB];           // pass 1: row groups per KV head
+  int32_t rg[MAXB];           // pass 1 (fp32 wide rows): row groups per KV head
+  int32_t nrb[MAXB];          // pass 1 (few-rows kernel): row blocks per KV head
   int32_t nc[MAXB];           // pass 1: key chunks per row group
-  int32_t kc[MAXB];           // pass 1: keys per chunk (multiple of 32)
+  int32_t kc[MAXB];           // keys per chunk (multiple of 32); 0 in the combine: every chunk
   int32_t prow[MAXB];         // pass 1: packed-row pitch per KV head of the partials
   float a[MAXB];              // forgetting-curve slope
   float c[MAXB];              // N - b - 0.5 (exact in fp32)

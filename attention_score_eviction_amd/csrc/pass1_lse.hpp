@@ -202,7 +202,7 @@ lse_combine_kernel(const CombineArgs args) {
   const int g = h * G + (r - j * G);
   const int q = q0 + j;
   const int nc = tab.nc[p];
-  const int last = q / tab.kc[p];
+  const int last = tab.kc[p] > 0 ? q / tab.kc[p] : nc - 1;  // kc 0: every chunk wrote every row
   const float2* pp = args.part + tab.ws0[p] + ((int64_t)h * tab.prow[p] + r) * nc;
   float mx = -INFINITY;
   for (int c = 0; c <= last; ++c) mx = fmaxf(mx, pp[c].x);

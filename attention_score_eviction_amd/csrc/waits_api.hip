@@ -14,6 +14,7 @@
 #include "pass1_lse.hpp"
 #include "pass2_colsum.hpp"
 #include "few_rows.hpp"
+#include "key_blocks.hpp"
 #include "select_compact.hpp"
 
 namespace waits {
@@ -29,12 +30,27 @@ constexpr int MAX_SEQ_LEN = (1 << 22) - 1;        // keeps N - b - 0.5 exact in 
 constexpr int MAX_B = 1 << 22;
 constexpr float LIVE_EXP_LIMIT = 89.0f;           // expf overflows above ~88.7228
 constexpr int FR_MIN_CHUNK = 256;                 // few-rows: shortest key chunk
+constexpr int BIG_MIN_CHUNK = 1024;               // row blocks: shortest pass-1 key chunk
+constexpr int KB_MIN_ROWS = 256;                  // key blocks: fewest rows per chunk
+constexpr int KB_MAX_CHUNKS = 64;                 // key blocks: most row chunks
+constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chunk (< 2^31)
+
+// How a sequence's two passes run.
+enum class Mode {
+  NONE,   // no tokens
+  FR,     // all packed rows of a KV head in one workgroup: few-rows kernel, both passes
+  BIG,    // more rows: pass 1 on the few-rows kernel in row blocks, pass 2 on key blocks
+  WIDE,   // fp32 rows of head_dim 128 (too wide for those register budgets): lse/colsum kernels
+};
 
 struct Seq {
   int n = 0, q0 = 0, pr = 0;
-  bool fr = false;            // both passes on the few-rows kernels
-  int rg = 0;                 // general pass 1: row groups per KV head
-  int nc = 1, kc = 32;        // key chunks (pass 1 split; few-rows: both passes)
+  Mode mode = Mode::NONE;
+  int rg = 0;                 // WIDE pass 1: row groups per KV head
+  int nrb = 0;                // FR / BIG pass 1: row blocks of FR_ROWS packed rows
+  int nkb = 0;                // BIG pass 2: key blocks of KB_KEYS keys
+  int nrc = 1;                // BIG pass 2: row chunks per key block
+  int nc = 1, kc = 32;        // key chunks: pass 1 (every mode), pass 2 (FR)
   int64_t tok0 = 0;
   float a = 0.f, c = 0.f;
 };
@@ -98,17 +114,31 @@ int first_live_row(int n, float a, int32_t b) {
 
 int round32(int x) { return (x + 31) / 32 * 32; }
 
-// Launch plan.  A sequence goes to the few-rows kernels when all packed rows
-// of a KV head fit one workgroup; their key ranges are cut into chunks until
-// the batch has about one workgroup per compute unit.  The other sequences
-// use the general kernels; their pass-1 key range is split only when row
-// groups alone give too few workgroups.
+int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
+// Bytes from the first to the last byte of one token's rows of a query-head
+// group (the key-block kernel addresses a chunk of queries of all G heads
+// from one buffer base).
+int64_t group_span(const waits_shape* s) {
+  const int64_t e = elt_bytes(s->dtype);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  return ((int64_t)(G - 1) * s->q_stride_head + s->head_dim) * e;
+}
+
+// Launch plan.  A sequence whose packed rows fit one workgroup per KV head
+// runs both passes on the few-rows kernel, its key range cut into chunks
+// until the batch has about one workgroup per compute unit.  A longer one
+// runs pass 1 on the same kernel in row blocks (key chunks for balance) and
+// pass 2 on key blocks (row chunks for balance).  Every chunk a buffer load
+// addresses spans less than 2^31 bytes.
 std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b) {
   const int G = s->n_q_heads / s->n_kv_heads;
-  // fp32 inputs at head_dim 128 would not fit the few-rows register budget
+  const int hkv = s->n_kv_heads;
   const bool fr_ok = !(s->dtype == WAITS_F32 && s->head_dim == 128);
+  const int64_t krow = std::max<int64_t>(1, s->kv_stride_tok * elt_bytes(s->dtype));
+  const int64_t qrow = std::max<int64_t>(1, s->q_stride_tok * elt_bytes(s->dtype));
   std::vector<Seq> v(s->batch);
-  int64_t fr_units = 0, gen_rg = 0;
+  int64_t fr_units = 0, big_units1 = 0, big_units2 = 0, wide_rg = 0;
   for (int i = 0; i < s->batch; ++i) {
     Seq& q = v[i];
     q.n = (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]);
@@ -117,28 +147,50 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
     q.c = (float)q.n - (float)(b ? b[i] : 1) - 0.5f;
     q.q0 = a ? first_live_row(q.n, a[i], b[i]) : 0;
     q.pr = G * (q.n - q.q0);
-    // few-rows kernels address a sequence's K span with 32-bit buffer offsets
-    const bool span_ok = (int64_t)q.n * s->kv_stride_tok * elt_bytes(s->dtype) < (int64_t(1) << 31);
-    q.fr = fr_ok && span_ok && q.n > 0 && q.pr <= FR_ROWS;
-    q.rg = q.fr ? 0 : (q.pr + WGROWS1 - 1) / WGROWS1;
     q.nc = 1;
     q.kc = std::max(32, round32(q.n));
-    if (q.fr) fr_units += s->n_kv_heads;
-    else gen_rg += (int64_t)s->n_kv_heads * q.rg;
-  }
-  if (fr_units > 0) {
-    const int want = (int)std::max<int64_t>(1, (NUM_CU + fr_units - 1) / fr_units);
-    for (Seq& q : v) {
-      if (!q.fr) continue;
-      const int nc = std::max(1, std::min(want, (q.n + FR_MIN_CHUNK - 1) / FR_MIN_CHUNK));
-      q.kc = round32((q.n + nc - 1) / nc);
-      q.nc = (q.n + q.kc - 1) / q.kc;
+    if (q.n == 0) {
+      q.mode = Mode::NONE;
+    } else if (!fr_ok) {
+      q.mode = Mode::WIDE;
+      q.rg = (q.pr + WGROWS1 - 1) / WGROWS1;
+      wide_rg += (int64_t)hkv * q.rg;
+    } else if (q.pr <= FR_ROWS) {
+      q.mode = Mode::FR;
+      q.nrb = 1;
+      fr_units += hkv;
+    } else {
+      q.mode = Mode::BIG;
+      q.nrb = (q.pr + FR_ROWS - 1) / FR_ROWS;
+      q.nkb = (q.n + KB_KEYS - 1) / KB_KEYS;
+      big_units1 += (int64_t)hkv * q.nrb;
+      big_units2 += (int64_t)hkv * q.nkb;
     }
   }
-  if (gen_rg > 0 && gen_rg < 2 * NUM_CU) {
-    const int want = (int)((4 * NUM_CU + gen_rg - 1) / gen_rg);
+  for (Seq& q : v) {
+    if (q.mode == Mode::FR) {
+      const int64_t want = std::max<int64_t>(1, ceil_div(NUM_CU, fr_units));
+      int64_t nc = std::max<int64_t>(1, std::min<int64_t>(want, ceil_div(q.n, FR_MIN_CHUNK)));
+      nc = std::max(nc, ceil_div(q.n * krow, SPAN_BYTES));
+      q.kc = round32((int)ceil_div(q.n, nc));
+      q.nc = (q.n + q.kc - 1) / q.kc;
+    } else if (q.mode == Mode::BIG) {
+      // pass 1: key chunks of each row block (sized in the kernel)
+      const int64_t want1 = std::max<int64_t>(1, ceil_div(4 * NUM_CU, big_units1));
+      int64_t nc = std::max<int64_t>(1, std::min<int64_t>(want1, ceil_div(q.n, BIG_MIN_CHUNK)));
+      q.nc = (int)std::max(nc, ceil_div(q.n * krow, SPAN_BYTES));
+      q.kc = 0;
+      // pass 2: row chunks of each key block
+      const int64_t want2 = std::max<int64_t>(1, ceil_div(8 * NUM_CU, big_units2));
+      int64_t nrc = std::min<int64_t>({want2, KB_MAX_CHUNKS, ceil_div(q.pr, KB_MIN_ROWS)});
+      nrc = std::max<int64_t>(1, nrc);
+      q.nrc = (int)std::max(nrc, ceil_div((q.n - q.q0 + 1) * qrow, SPAN_BYTES - group_span(s)));
+    }
+  }
+  if (wide_rg > 0 && wide_rg < 2 * NUM_CU) {
+    const int want = (int)((4 * NUM_CU + wide_rg - 1) / wide_rg);
     for (Seq& q : v) {
-      if (q.fr || q.n == 0) continue;
+      if (q.mode != Mode::WIDE) continue;
       const int nc = std::max(1, std::min(want, (q.n + 511) / 512));
       q.kc = round32((q.n + nc - 1) / nc);
       q.nc = (q.n + q.kc - 1) / q.kc;
@@ -148,7 +200,7 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
 }
 
 // Pass-1 packed-row pitch of a sequence's partials (per KV head).
-int partial_rows(const Seq& q) { return q.fr ? FR_ROWS : q.rg * WGROWS1; }
+int partial_rows(const Seq& q) { return q.mode == Mode::WIDE ? q.rg * WGROWS1 : q.nrb * FR_ROWS; }
 
 // Partial (float2) slots pass 1 needs for sequences [lo, hi).
 int64_t partial_slots(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
@@ -165,6 +217,14 @@ size_t lse_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
   return (size_t)mx * sizeof(float2);
 }
 
+// Pass-2 partial sums: [row chunk][Hkv][T] fp32 for the most-split sequence.
+size_t colsum_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+  int mx = 0;
+  for (const Seq& q : v)
+    if (q.mode == Mode::BIG && q.nrc > 1) mx = std::max(mx, q.nrc);
+  return (size_t)mx * s->n_kv_heads * (size_t)s->cu_seqlens[s->batch] * sizeof(float);
+}
+
 size_t lse_buffer_bytes(const waits_shape* s) {
   const size_t bytes = (size_t)s->n_q_heads * (size_t)s->cu_seqlens[s->batch] * sizeof(float);
   return (bytes + 255) / 256 * 256;
@@ -179,6 +239,7 @@ void fill_table(SeqTable& t, const std::vector<Seq>& v, int lo, int hi, int hkv)
     t.n[j] = q.n;
     t.q0[j] = q.q0;
     t.rg[j] = q.rg;
+    t.nrb[j] = q.nrb;
     t.nc[j] = q.nc;
     t.kc[j] = q.kc;
     t.prow[j] = partial_rows(q);
@@ -261,7 +322,7 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     int fr_items = 0;
     for (int i = lo; i < hi; ++i) {
       f.tab.first[i - lo] = fr_items;
-      if (v[i].fr) fr_items += hkv * v[i].nc;
+      if (v[i].mode == Mode::FR || v[i].mode == Mode::BIG) fr_items += hkv * v[i].nrb * v[i].nc;
     }
     f.tab.first[hi - lo] = fr_items;
     if (fr_items > 0) {
@@ -269,7 +330,7 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
 
-    // general sequences
+    // fp32 rows of head_dim 128
     LseArgs args;
     args.q = q;
     args.k = k;
@@ -285,17 +346,11 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     int items = 0;
     for (int i = lo; i < hi; ++i) {
       args.tab.first[i - lo] = items;
-      if (!v[i].fr) items += hkv * v[i].rg * v[i].nc;
+      if (v[i].mode == Mode::WIDE) items += hkv * v[i].rg * v[i].nc;
     }
     args.tab.first[hi - lo] = items;
     if (items > 0) {
-      if (s->dtype == WAITS_BF16) {
-        if (s->head_dim == 64) launch_lse<bf16_t, 64>(args, items, stream);
-        else launch_lse<bf16_t, 128>(args, items, stream);
-      } else {
-        if (s->head_dim == 64) launch_lse<float, 64>(args, items, stream);
-        else launch_lse<float, 128>(args, items, stream);
-      }
+      launch_lse<float, 128>(args, items, stream);
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
 
@@ -311,6 +366,9 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     for (int i = lo; i < hi; ++i) {
       cargs.tab.first[i - lo] = rows;
       if (v[i].nc > 1) rows += hkv * v[i].pr;
+      // the few-rows kernel writes every (row, chunk) partial; the lse kernel
+      // only the chunks a row reaches
+      if (v[i].mode != Mode::WIDE) cargs.tab.kc[i - lo] = 0;
     }
     cargs.tab.first[hi - lo] = rows;
     if (rows > 0) {
@@ -322,8 +380,13 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
 }
 
 int run_colsum(const waits_shape* s, const void* q, const void* k, const float* lse,
-               const float* a, const int32_t* b, float* scores, hipStream_t stream) {
+               const float* a, const int32_t* b, float* scores, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, a, b);
+  for (const Seq& sq : v)
+    if (sq.mode == Mode::BIG && group_span(s) > SPAN_BYTES / 2) return WAITS_EUNSUPPORTED;
+  const size_t need = colsum_ws_bytes(s, v);
+  if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 4)))) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;
   const int hkv = s->n_kv_heads;
   for (int lo = 0; lo < s->batch; lo += MAXB) {
@@ -331,6 +394,7 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
     SeqTable tab;
     fill_table(tab, v, lo, hi, hkv);
 
+    // few-rows sequences
     FrArgs f = fr_args(s, q, k);
     f.lse = const_cast<float*>(lse);
     f.scores = scores;
@@ -338,7 +402,7 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
     int fr_items = 0;
     for (int i = lo; i < hi; ++i) {
       f.tab.first[i - lo] = fr_items;
-      if (v[i].fr) fr_items += hkv * v[i].nc;
+      if (v[i].mode == Mode::FR) fr_items += hkv * v[i].nc;
     }
     f.tab.first[hi - lo] = fr_items;
     if (fr_items > 0) {
@@ -346,6 +410,55 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
 
+    // key blocks of the longer sequences
+    BlockArgs kbargs;
+    kbargs.q = q;
+    kbargs.k = k;
+    kbargs.lse = lse;
+    kbargs.scores = scores;
+    kbargs.part = static_cast<float*>(ws);
+    kbargs.st = strides_of(s);
+    kbargs.T = s->cu_seqlens[s->batch];
+    kbargs.G = G;
+    kbargs.hkv = hkv;
+    kbargs.scale_log2 = s->scale * LOG2E;
+    kbargs.tab = tab;
+    ReduceArgs rargs;
+    rargs.part = static_cast<const float*>(ws);
+    rargs.scores = scores;
+    rargs.T = kbargs.T;
+    rargs.hkv = hkv;
+    rargs.tab = tab;
+    int kb_items = 0, red_items = 0;
+    for (int i = lo; i < hi; ++i) {
+      kbargs.tab.first[i - lo] = kb_items;
+      kbargs.tab.nc[i - lo] = v[i].nrc;
+      rargs.tab.first[i - lo] = red_items;
+      rargs.tab.nc[i - lo] = v[i].nrc;
+      if (v[i].mode == Mode::BIG) {
+        kb_items += hkv * v[i].nkb * v[i].nrc;
+        if (v[i].nrc > 1) red_items += hkv * v[i].n;
+      }
+    }
+    kbargs.tab.first[hi - lo] = kb_items;
+    rargs.tab.first[hi - lo] = red_items;
+    if (kb_items > 0) {
+      if (s->dtype == WAITS_BF16) {
+        if (s->head_dim == 64)
+          hipLaunchKernelGGL((key_block_kernel<bf16_t, 64>), dim3(kb_items), dim3(KB_THREADS), 0, stream, kbargs);
+        else
+          hipLaunchKernelGGL((key_block_kernel<bf16_t, 128>), dim3(kb_items), dim3(KB_THREADS), 0, stream, kbargs);
+      } else {  // fp32 only at head_dim 64 (see plan_seqs)
+        hipLaunchKernelGGL((key_block_kernel<float, 64>), dim3(kb_items), dim3(KB_THREADS), 0, stream, kbargs);
+      }
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+    if (red_items > 0) {
+      hipLaunchKernelGGL(colsum_reduce_kernel, dim3((red_items + 255) / 256), dim3(256), 0, stream, rargs);
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    }
+
+    // fp32 rows of head_dim 128
     ColsumArgs args;
     args.q = q;
     args.k = k;
@@ -360,17 +473,11 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
     int items = 0;
     for (int i = lo; i < hi; ++i) {
       args.tab.first[i - lo] = items;
-      if (!v[i].fr) items += hkv * ((v[i].n + WGKEYS2 - 1) / WGKEYS2);
+      if (v[i].mode == Mode::WIDE) items += hkv * ((v[i].n + WGKEYS2 - 1) / WGKEYS2);
     }
     args.tab.first[hi - lo] = items;
     if (items > 0) {
-      if (s->dtype == WAITS_BF16) {
-        if (s->head_dim == 64) launch_colsum<bf16_t, 64>(args, items, stream);
-        else launch_colsum<bf16_t, 128>(args, items, stream);
-      } else {
-        if (s->head_dim == 64) launch_colsum<float, 64>(args, items, stream);
-        else launch_colsum<float, 128>(args, items, stream);
-      }
+      launch_colsum<float, 128>(args, items, stream);
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
   }
@@ -495,12 +602,24 @@ int waits_lse_workspace_bytes(const waits_shape* s, const float* a, const int32_
   return WAITS_OK;
 }
 
+int waits_colsum_workspace_bytes(const waits_shape* s, const float* a, const int32_t* b,
+                                 size_t* bytes) {
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
+  if (rc != WAITS_OK) return rc;
+  *bytes = colsum_ws_bytes(s, plan_seqs(s, a, b));
+  return WAITS_OK;
+}
+
 int waits_score_workspace_bytes(const waits_shape* s, const float* a, const int32_t* b,
                                 size_t* bytes) {
-  size_t part = 0;
-  const int rc = waits_lse_workspace_bytes(s, a, b, &part);
+  int rc = check_shape(s, true);
+  if (rc == WAITS_OK) rc = check_curves(s, a, b);
+  if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
   if (rc != WAITS_OK) return rc;
-  *bytes = lse_buffer_bytes(s) + part;
+  const std::vector<Seq> v = plan_seqs(s, a, b);
+  *bytes = lse_buffer_bytes(s) + std::max(lse_ws_bytes(s, v), colsum_ws_bytes(s, v));
   return WAITS_OK;
 }
 
@@ -516,7 +635,8 @@ int waits_lse(const waits_shape* s, const void* q, const void* k, const float* a
 }
 
 int waits_colsum(const waits_shape* s, const void* q, const void* k, const float* lse,
-                 const float* a, const int32_t* b, float* scores, hipStream_t stream) {
+                 const float* a, const int32_t* b, float* scores, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   int rc = check_shape(s, true);
   if (rc == WAITS_OK) rc = check_curves(s, a, b);
   if (rc != WAITS_OK) return rc;
@@ -524,7 +644,7 @@ int waits_colsum(const waits_shape* s, const void* q, const void* k, const float
   if (!q || !k || !lse || !scores || !is_aligned(q, 16) || !is_aligned(k, 16) ||
       !is_aligned(lse, 4) || !is_aligned(scores, 4))
     return WAITS_EINVAL;
-  return run_colsum(s, q, k, lse, a, b, scores, stream);
+  return run_colsum(s, q, k, lse, a, b, scores, ws, ws_bytes, stream);
 }
 
 int waits_score(const waits_shape* s, const void* q, const void* k, const float* a,
@@ -537,13 +657,13 @@ int waits_score(const waits_shape* s, const void* q, const void* k, const float*
     return WAITS_EINVAL;
   const std::vector<Seq> v = plan_seqs(s, a, b);
   const size_t lse_bytes = lse_buffer_bytes(s);
-  const size_t need = lse_bytes + lse_ws_bytes(s, v);
+  const size_t need = lse_bytes + std::max(lse_ws_bytes(s, v), colsum_ws_bytes(s, v));
   if (!ws || ws_bytes < need || !is_aligned(ws, 256)) return WAITS_EWORKSPACE;
   float* lse = static_cast<float*>(ws);
-  void* part = static_cast<unsigned char*>(ws) + lse_bytes;
+  void* part = static_cast<unsigned char*>(ws) + lse_bytes;  // pass-1 partials, then pass-2 partials
   rc = run_lse(s, q, k, a, b, lse, part, ws_bytes - lse_bytes, stream);
   if (rc != WAITS_OK) return rc;
-  return run_colsum(s, q, k, lse, a, b, scores, stream);
+  return run_colsum(s, q, k, lse, a, b, scores, part, ws_bytes - lse_bytes, stream);
 }
 
 int waits_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,

@@ -61,7 +61,8 @@ _SIGS = {
     "waits_lse_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
     "waits_score_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
     "waits_lse": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
-    "waits_colsum": [_SP, _P, _P, _P, _FP, _IP, _P, _P],
+    "waits_colsum_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
+    "waits_colsum": [_SP, _P, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
     "waits_score": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
     "waits_select": [_SP, _P, ctypes.c_int32, _P, _P],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
@@ -189,6 +190,14 @@ def lse_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
     return out.value
 
 
+def colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    out = ctypes.c_size_t(0)
+    _check("waits_colsum_workspace_bytes",
+           lib().waits_colsum_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
+    return out.value
+
+
 def score_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
     m = _Marshal(cu_seqlens, q, k, scale, a, b)
     out = ctypes.c_size_t(0)
@@ -224,14 +233,18 @@ def lse(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
 
 
 def colsum(q: torch.Tensor, k: torch.Tensor, lse_rows: torch.Tensor, cu_seqlens, a, b,
-           scale=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+           scale=None, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Pass 2: WAITS key scores [Hkv, T] fp32 from the pass-1 normalisers."""
     _last_dim_contiguous(q, k)
     m = _Marshal(cu_seqlens, q, k, scale, a, b)
     if out is None:
         out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
+    nbytes = colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale)
+    ws = _workspace(nbytes, q.device, workspace)
     _check("waits_colsum", lib().waits_colsum(
-        m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), _stream(q)))
+        m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), _ptr(ws),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
     return out
 
 

@@ -233,7 +233,8 @@ def main():
     B = len(wl["lengths"])
 
     lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
-    ws_bytes = W.waits.lse_workspace_bytes(q, k, cu, a, b)
+    ws_bytes = max(W.waits.lse_workspace_bytes(q, k, cu, a, b),
+                   W.waits.colsum_workspace_bytes(q, k, cu, a, b))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     scores = torch.empty((hkv, T), dtype=torch.float32, device=dev)
     idx = torch.empty((B, hkv, budget), dtype=torch.int32, device=dev)
@@ -247,7 +248,7 @@ def main():
         if e: e[0].record(stream)
         W.lse(q, k, cu, a, b, out=lse, workspace=ws)
         if e: e[1].record(stream)
-        W.colsum(q, k, lse, cu, a, b, out=scores)
+        W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws)
         if e: e[2].record(stream)
         W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc)  # one launch
         if e: e[3].record(stream)

@@ -109,19 +109,28 @@ int waits_lse(const waits_shape* shape, const void* q, const void* k,
               const float* a, const int32_t* b, float* lse, void* workspace,
               size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace waits_colsum needs for this batch (0 is possible). */
+int waits_colsum_workspace_bytes(const waits_shape* shape, const float* a,
+                                 const int32_t* b, size_t* bytes);
+
 /*
  * Pass 2, weighted column sums (README introduction: accumulative attention
  * score under the forgetting curve):
  *   scores[h * T + t0 + k] = sum_{g in group h} sum_{q >= k}
  *                            w[q] * exp(scale <Q[t0+q, g], K[t0+k, h]> - lse[g*T+t0+q])
  * for every key k of every sequence.  lse: as written by waits_lse.
- * scores: device fp32 [n_kv_heads, T], fully written.
+ * scores: device fp32 [n_kv_heads, T], fully written.  workspace: device,
+ * 4-byte aligned, >= waits_colsum_workspace_bytes (partial sums of keys
+ * whose rows are split over several workgroups; they are added in a fixed
+ * order, so scores are bitwise reproducible).
  */
 int waits_colsum(const waits_shape* shape, const void* q, const void* k,
                  const float* lse, const float* a, const int32_t* b,
-                 float* scores, hipStream_t stream);
+                 float* scores, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
 
-/* Bytes of device workspace waits_score needs (lse buffer + pass-1 workspace). */
+/* Bytes of device workspace waits_score needs: the lse buffer, then room
+ * for the larger of the pass-1 and pass-2 workspaces. */
 int waits_score_workspace_bytes(const waits_shape* shape, const float* a,
                                 const int32_t* b, size_t* bytes);
 

@@ -155,11 +155,34 @@ def test_first_rows_match_survey_live_counts():
 def test_workspace_sizes():
     q = torch.empty((4096, 32, 64), dtype=torch.bfloat16)
     k = torch.empty((4096, 8, 64), dtype=torch.bfloat16)
-    # all rows live: plenty of row groups, no key split, no partials
-    assert W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1]) == 0
-    # 105 live rows: key range split into chunks with (max, sum) partials
+    # 105 live rows (one workgroup per KV head): key range split into chunks
+    # with (max, sum) partials; pass 2 writes its scores directly
     assert W.lse_workspace_bytes(q, k, [0, 4096], [1.0], [16]) > 0
-    assert W.score_workspace_bytes(q, k, [0, 4096], [0.0], [1]) >= 32 * 4096 * 4
+    assert W.colsum_workspace_bytes(q, k, [0, 4096], [1.0], [16]) == 0
+    # all rows live, one short sequence: too few row blocks / key blocks for
+    # the chip, so pass 1 splits keys and pass 2 splits rows (partial sums
+    # [chunk][Hkv][T] fp32)
+    lse_ws = W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1])
+    col_ws = W.colsum_workspace_bytes(q, k, [0, 4096], [0.0], [1])
+    assert lse_ws > 0 and col_ws > 0 and col_ws % (8 * 4096 * 4) == 0
+    assert (W.score_workspace_bytes(q, k, [0, 4096], [0.0], [1])
+            >= 32 * 4096 * 4 + max(lse_ws, col_ws))
+
+
+def test_colsum_workspace_validation():
+    s = _shape(n=4096, hq=32, hkv=8)
+    a, b = _ab(a=0.0, b=1)
+    need = ctypes.c_size_t(0)
+    assert W.lib().waits_colsum_workspace_bytes(ctypes.byref(s), a.ctypes.data_as(W._FP),
+                                                b.ctypes.data_as(W._IP), ctypes.byref(need)) == 0
+    assert need.value > 0
+
+    def colsum(ws, nbytes):
+        return W.lib().waits_colsum(ctypes.byref(s), FAKE, FAKE, FAKE, a.ctypes.data_as(W._FP),
+                                    b.ctypes.data_as(W._IP), FAKE, ws, nbytes, None)
+    assert colsum(None, 0) == W.WAITS_EWORKSPACE
+    assert colsum(FAKE, need.value - 1) == W.WAITS_EWORKSPACE
+    assert colsum(ctypes.c_void_p(0x100002), need.value) == W.WAITS_EWORKSPACE  # misaligned
 
 
 def test_binding_raises_without_library(monkeypatch):

@@ -221,16 +221,26 @@ def test_uniform_attention_closed_form_on_gpu():
     np.testing.assert_allclose(s, g / 2 * (harm[n] - harm[:n]), rtol=2e-5)
 
 
-def test_head_major_strides_match_token_major():
-    _say("head-major strides")
+@pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1)])
+def test_head_major_strides_match_token_major(a, b):
+    # a=1: one workgroup holds all rows; a=0: row blocks and key blocks
+    _say(f"head-major strides a={a}")
     bt = make_prompt(21, 999, 8, 2, 128, heavy=True)
     q, k, v = to_device(bt)
     qh = q.permute(1, 0, 2).contiguous().permute(1, 0, 2)   # [T, H, d] view of [H, T, d]
     kh = k.permute(1, 0, 2).contiguous().permute(1, 0, 2)
     assert qh.stride(0) == 128 and kh.stride(1) == 999 * 128
-    s1 = W.score(q, k, bt.cu_seqlens, [1.0], [16])
-    s2 = W.score(qh, kh, bt.cu_seqlens, [1.0], [16])
+    s1 = W.score(q, k, bt.cu_seqlens, [a], [b])
+    s2 = W.score(qh, kh, bt.cu_seqlens, [a], [b])
     assert torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1), (0.01, 128)])
+def test_fp32_head_dim_128(a, b):
+    # fp32 rows of 512 bytes take the row-group / key-group kernels
+    _say(f"fp32 d=128 a={a} b={b}")
+    bt = make_batch([41, 42], [700, 1500], 4, 2, 128, heavy=True, dtype="f32")
+    _full_check(bt, [a, a], [b, b], 128)
 
 
 def test_deterministic_and_causal_support():
