@@ -158,8 +158,16 @@ def cpu_baseline(wl, budget_s: float):
 
 
 KERNEL_SOURCES = ("attention_score_eviction_amd/csrc/few_rows.hpp",
+                  "attention_score_eviction_amd/csrc/key_blocks.hpp",
+                  "attention_score_eviction_amd/csrc/select_compact.hpp",
                   "attention_score_eviction_amd/csrc/device_common.hpp",
                   "attention_score_eviction_amd/csrc/kernel_args.hpp")
+
+# Bench kernel names and a substring of the device symbol each launches (the
+# timed kernel; pass 1 may add the small combine kernel, which is not counted).
+KERNEL_SYMBOLS = {"pass1_lse": ("few_rows_kernel", "false"),
+                  "pass2_colsum": ("few_rows_kernel", "true"),
+                  "select_compact": ("select_kernel", "true")}
 
 
 def kernel_source_hash() -> str:
@@ -199,6 +207,72 @@ def copy_calibration(nbytes: int, reps: int = 3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _counter_means(run_dir: str, counter: str):
+    """Mean counter value per dispatch, by kernel symbol, from a rocprofv3
+    --pmc csv run directory."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                k = row["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def _trace_means(run_dir: str):
+    """Mean duration (ns) per kernel symbol from a rocprofv3 kernel-trace csv."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                out[row["Name"]] = float(row["AverageNs"])
+    return out
+
+
+def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
+    """Write profiles/traffic_<workload>.json from rocprofv3 runs under
+    prof_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE over bench.py),
+    cfetch/ and cwrite/ (the same over --copy-calibration copy_bytes), trace/
+    (kernel trace).  The counters, in KiB per dispatch, are scaled by what
+    they read for the copy, whose bytes are known."""
+    def pick(means, name):
+        base, flag = KERNEL_SYMBOLS[name]
+        hits = [k for k in means if base in k and (f", {flag}," in k or f", {flag}>" in k)]
+        return max(hits, key=lambda k: means[k]) if hits else None
+    fetch = _counter_means(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(prof_dir, "write"), "WRITE_SIZE")
+    cfetch = max(_counter_means(os.path.join(prof_dir, "cfetch"), "FETCH_SIZE").values())
+    cwrite = max(_counter_means(os.path.join(prof_dir, "cwrite"), "WRITE_SIZE").values())
+    trace = _trace_means(os.path.join(prof_dir, "trace"))
+    ff, wf = copy_bytes / (cfetch * 1024.0), copy_bytes / (cwrite * 1024.0)
+    rec = {"workload": workload(workload_name)["desc"], "source_hash": kernel_source_hash(),
+           "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                                "fetch_kib": cfetch, "write_kib": cwrite,
+                                "fetch_factor": ff, "write_factor": wf},
+           "kernels": {}}
+    for name in KERNEL_SYMBOLS:
+        sym = pick(fetch, name)
+        if sym is None:
+            continue
+        rd = fetch[sym] * 1024.0 * ff
+        wr = write.get(sym, 0.0) * 1024.0 * wf
+        rec["kernels"][name] = {"symbol": sym, "fetch_kib_raw": fetch[sym],
+                                "write_kib_raw": write.get(sym), "hbm_read_bytes": rd,
+                                "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
+                                "avg_duration_ns": trace.get(sym)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,9 +283,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="only write profiles/traffic_<workload>.json from rocprofv3 runs in DIR "
+                         "(fetch/, write/, cfetch/, cwrite/, trace/) and exit; no GPU needed")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.counters_from:
+        counters_from(args.counters_from, args.workload, 1 << 30)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the WAITS path needs no collectives and this "
