@@ -39,7 +39,7 @@
 namespace waits {
 
 constexpr int FR_ROWS = 512;                          // packed rows per workgroup
-constexpr int FR_SUB = 2;                             // 32-key sub-tiles per stage
+constexpr int FR_SUB = 4;                             // 32-key sub-tiles per stage
 constexpr int FR_STAGE = FR_SUB * TILE;               // keys per stage (one barrier)
 constexpr int FR_RING = 2;                            // stages of loads in flight
 
@@ -69,11 +69,13 @@ few_rows_kernel(const FrArgs args) {
   constexpr int CPR = Geo::ROW_BYTES / 16;                    // 16-byte chunks per K row
   constexpr int CHUNKS = FR_STAGE * CPR;                       // per stage
   constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;   // chunks per thread per stage
-  static_assert(FR_SUB == 2, "accumulator parity follows the sub-tile index");
+  static_assert(FR_SUB % 2 == 0, "accumulator parity follows the sub-tile index");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float row_off[FR_ROWS];   // pass 2: exponent offsets
   __shared__ __attribute__((aligned(16))) int row_q[FR_ROWS];       // row position (-1: padding)
-  __shared__ float red[4][FR_WAVES][TILE];                         // pass 2: per-wave key sums
+  // pass 2: per-wave key sums of a sub-tile; 2 FR_SUB slots, so one stage's
+  // stores never meet the previous stage's flushes
+  __shared__ float red[2 * FR_SUB][FR_WAVES][TILE];
 
   const SeqTable& tab = args.tab;
   const int item = blockIdx.x;
@@ -351,14 +353,14 @@ few_rows_kernel(const FrArgs args) {
   // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)
   auto red_store = [&](int j, float csum) {
     csum += wave_xor32(csum);
-    if (hf == 0) red[j & 3][wave][col] = csum;
+    if (hf == 0) red[j & (2 * FR_SUB - 1)][wave][col] = csum;
   };
   auto flush = [&](int j) {
     if (j >= 0 && j < nsub && tid < TILE) {
       const int key = kbeg + j * TILE + tid;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & 3][w][tid];
+      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][tid];
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
     }
   };
@@ -425,7 +427,7 @@ few_rows_kernel(const FrArgs args) {
       const int buf = (1 + s) & 1;  // == st & 1
       if constexpr (PASS2) {
 #pragma unroll
-        for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 3);  // previous stage's epilogues
+        for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - FR_SUB - 1);  // previous stage's epilogues
       }
 #pragma unroll
       for (int u = 0; u < FR_SUB; ++u) subtile(buf, u, st * FR_SUB + u);
