@@ -38,9 +38,7 @@
 
 namespace waits {
 
-constexpr int FR_ROWS = 512;                          // packed rows per workgroup
-constexpr int FR_SUB = 4;                             // 32-key sub-tiles per stage
-constexpr int FR_STAGE = FR_SUB * TILE;               // keys per stage (one barrier)
+constexpr int FR_ROWS = 512;                          // packed rows of the largest workgroup
 constexpr int FR_RING = 2;                            // stages of loads in flight
 
 struct FrArgs {
@@ -58,12 +56,19 @@ struct FrArgs {
   SeqTable tab;               // nc / kc: key chunks; first[]: items
 };
 
-// FR_WAVES waves, each owning FR_TW row tiles (FR_WAVES * FR_TW * 32 == FR_ROWS).
+// FR_WAVES waves, each owning FR_TW row tiles: ROWS = FR_WAVES * FR_TW * 32
+// packed rows per workgroup (a head with fewer rows takes the smallest
+// workgroup that holds them, so short windows do not pad to FR_ROWS).
 template <typename T, int D, bool PASS2, int FR_WAVES, int FR_TW>
 __global__ void __launch_bounds__(FR_WAVES * WAVE)
 few_rows_kernel(const FrArgs args) {
   constexpr int FR_THREADS = FR_WAVES * WAVE;
-  static_assert(FR_WAVES * FR_TW * TILE == FR_ROWS, "one workgroup holds FR_ROWS rows");
+  constexpr int ROWS = FR_WAVES * FR_TW * TILE;
+  static_assert(ROWS <= FR_ROWS, "at most FR_ROWS rows per workgroup");
+  // 32-key sub-tiles per stage (one barrier each); smaller workgroups take
+  // shorter stages to keep each thread's share of the load ring small
+  constexpr int FR_SUB = FR_WAVES >= 8 ? 4 : 2;
+  constexpr int FR_STAGE = FR_SUB * TILE;
   using Geo = TileGeom<T, D>;
   constexpr int HALF = Geo::ROW_BYTES / 2;
   constexpr int CPR = Geo::ROW_BYTES / 16;                    // 16-byte chunks per K row
@@ -71,8 +76,8 @@ few_rows_kernel(const FrArgs args) {
   constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;   // chunks per thread per stage
   static_assert(FR_SUB % 2 == 0, "accumulator parity follows the sub-tile index");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float row_off[FR_ROWS];   // pass 2: exponent offsets
-  __shared__ __attribute__((aligned(16))) int row_q[FR_ROWS];       // row position (-1: padding)
+  __shared__ __attribute__((aligned(16))) float row_off[ROWS];   // pass 2: exponent offsets
+  __shared__ __attribute__((aligned(16))) int row_q[ROWS];       // row position (-1: padding)
   // pass 2: per-wave key sums of a sub-tile; 2 FR_SUB slots, so one stage's
   // stores never meet the previous stage's flushes
   __shared__ float red[2 * FR_SUB][FR_WAVES][TILE];
@@ -90,7 +95,7 @@ few_rows_kernel(const FrArgs args) {
   const int N = tab.n[p], q0 = tab.q0[p];
   const int PR = G * (N - q0);
   const int64_t tok0 = tab.tok0[p];
-  const int rbase = rb * FR_ROWS;             // first packed row of the block
+  const int rbase = rb * ROWS;                // first packed row of the block
   const int qb0 = q0 + rbase / G;             // its first query
   // Keys: pass 2 (one row block) the sequence's keys in chunks of kc; pass 1
   // the keys up to the block's last query, cut into nc chunks.
@@ -99,7 +104,7 @@ few_rows_kernel(const FrArgs args) {
     kbeg = chunk * tab.kc[p];
     kend = min(kbeg + tab.kc[p], N);
   } else {
-    const int nkeys = min(N, q0 + (min(rbase + FR_ROWS, PR) - 1) / G + 1);
+    const int nkeys = min(N, q0 + (min(rbase + ROWS, PR) - 1) / G + 1);
     const int kc = ((nkeys + nc - 1) / nc + TILE - 1) / TILE * TILE;
     kbeg = chunk * kc;
     kend = min(kbeg + kc, nkeys);
@@ -116,7 +121,7 @@ few_rows_kernel(const FrArgs args) {
 
   if constexpr (!PASS2) {
     if (kbeg >= kend) {  // a chunk past the block's keys: its partials are empty
-      for (int r = tid; r < FR_ROWS && rbase + r < PR; r += FR_THREADS)
+      for (int r = tid; r < ROWS && rbase + r < PR; r += FR_THREADS)
         args.part[tab.ws0[p] + ((int64_t)h * tab.prow[p] + rbase + r) * nc + chunk] =
             make_float2(-INFINITY, 0.f);
       return;
@@ -124,7 +129,7 @@ few_rows_kernel(const FrArgs args) {
   }
 
   // Row table (and pass-2 exponent offsets): one thread per packed row.
-  for (int r = tid; r < FR_ROWS; r += FR_THREADS) {
+  for (int r = tid; r < ROWS; r += FR_THREADS) {
     int q = -1;
     float off = INFINITY;
     if (rbase + r < PR) {
@@ -343,11 +348,18 @@ few_rows_kernel(const FrArgs args) {
     for (int v = 0; v < Geo::NV; ++v) kf[v] = ld16(krow + 16 * v);
   };
   auto mma_both = [&](f32x16* acc, const u32x4* kf) {
+    if constexpr (FR_TW == 1) {
+      acc[0] = f32x16{};
+      if constexpr (PASS2) mma_tile<T, D>(acc[0], qf[0], kf);
+      else mma_tile<T, D>(acc[0], kf, qf[0]);
+    } else {
+      static_assert(FR_TW % 2 == 0, "row tiles go in pairs");
 #pragma unroll
-    for (int t = 0; t < FR_TW; t += 2) {
-      acc[t] = f32x16{};
-      acc[t + 1] = f32x16{};
-      mma_tile2<T, D, !PASS2>(acc[t], acc[t + 1], qf[t], qf[t + 1], kf);
+      for (int t = 0; t < FR_TW; t += 2) {
+        acc[t] = f32x16{};
+        acc[t + 1] = f32x16{};
+        mma_tile2<T, D, !PASS2>(acc[t], acc[t + 1], qf[t], qf[t + 1], kf);
+      }
     }
   };
   // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)

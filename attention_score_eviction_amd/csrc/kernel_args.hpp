@@ -50,6 +50,7 @@ struct CombineArgs {
   int64_t T;
   int32_t G;
   int32_t hkv;
+  int32_t team;               // lanes per row (power of two dividing 64)
   SeqTable tab;               // first[] counts (KV head, packed row) pairs
 };
 

@@ -188,16 +188,21 @@ lse_kernel(const LseArgs args) {
 // or before its own position (later chunks hold no key of its causal range).
 __global__ void __launch_bounds__(256)
 lse_combine_kernel(const CombineArgs args) {
+  // A team of args.team lanes (a power of two dividing 64) merges one row's
+  // partials: each lane takes every team-th chunk, then the team reduces.
   const SeqTable& tab = args.tab;
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item >= tab.first[tab.nb]) return;
-  const int p = find_seq(tab.first, tab.nb, item);
+  const int team = args.team;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int item = gid / team;
+  const int tl = gid - item * team;
+  const bool live = item < tab.first[tab.nb];
+  const int p = find_seq(tab.first, tab.nb, live ? item : 0);
   const int local = item - tab.first[p];
   const int G = args.G;
   const int N = tab.n[p], q0 = tab.q0[p];
   const int PR = G * (N - q0);
-  const int h = local / PR;
-  const int r = local - h * PR;
+  const int h = live ? local / PR : 0;
+  const int r = live ? local - h * PR : 0;
   const int j = r / G;
   const int g = h * G + (r - j * G);
   const int q = q0 + j;
@@ -205,10 +210,14 @@ lse_combine_kernel(const CombineArgs args) {
   const int last = tab.kc[p] > 0 ? q / tab.kc[p] : nc - 1;  // kc 0: every chunk wrote every row
   const float2* pp = args.part + tab.ws0[p] + ((int64_t)h * tab.prow[p] + r) * nc;
   float mx = -INFINITY;
-  for (int c = 0; c <= last; ++c) mx = fmaxf(mx, pp[c].x);
+  if (live)
+    for (int c = tl; c <= last; c += team) mx = fmaxf(mx, pp[c].x);
+  for (int o = team / 2; o > 0; o /= 2) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
   float lt = 0.f;
-  for (int c = 0; c <= last; ++c) lt += pp[c].y * exp2f(pp[c].x - mx);
-  args.lse[(int64_t)g * args.T + tab.tok0[p] + q] = (mx + log2f(lt)) * LN2;
+  if (live && mx != -INFINITY)
+    for (int c = tl; c <= last; c += team) lt += pp[c].y * exp2f(pp[c].x - mx);
+  for (int o = team / 2; o > 0; o /= 2) lt += __shfl_xor(lt, o, WAVE);
+  if (live && tl == 0) args.lse[(int64_t)g * args.T + tab.tok0[p] + q] = (mx + log2f(lt)) * LN2;
 }
 
 }  // namespace waits

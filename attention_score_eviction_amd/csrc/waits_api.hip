@@ -35,6 +35,16 @@ constexpr int KB_MIN_ROWS = 256;                  // key blocks: fewest rows per
 constexpr int KB_MAX_CHUNKS = 64;                 // key blocks: most row chunks
 constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chunk (< 2^31)
 
+// Few-rows workgroup shapes: a head takes the smallest that holds its packed
+// rows (row blocks of longer heads use the largest).
+struct FrShape {
+  int rows, waves, tiles;
+};
+constexpr FrShape FR_SHAPES[] = {{64, 2, 1}, {128, 4, 1}, {256, 8, 1}, {512, 8, 2}};
+constexpr int FR_NSHAPES = 4;
+constexpr int FR_BIG_SHAPE = FR_NSHAPES - 1;
+static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the largest shape");
+
 // How a sequence's two passes run.
 enum class Mode {
   NONE,   // no tokens
@@ -47,7 +57,8 @@ struct Seq {
   int n = 0, q0 = 0, pr = 0;
   Mode mode = Mode::NONE;
   int rg = 0;                 // WIDE pass 1: row groups per KV head
-  int nrb = 0;                // FR / BIG pass 1: row blocks of FR_ROWS packed rows
+  int frs = FR_BIG_SHAPE;     // FR / BIG: few-rows workgroup shape (FR_SHAPES index)
+  int nrb = 0;                // FR / BIG pass 1: row blocks of that shape's rows
   int nkb = 0;                // BIG pass 2: key blocks of KB_KEYS keys
   int nrc = 1;                // BIG pass 2: row chunks per key block
   int nc = 1, kc = 32;        // key chunks: pass 1 (every mode), pass 2 (FR)
@@ -158,7 +169,9 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
     } else if (q.pr <= FR_ROWS) {
       q.mode = Mode::FR;
       q.nrb = 1;
-      fr_units += hkv;
+      q.frs = 0;
+      while (FR_SHAPES[q.frs].rows < q.pr) ++q.frs;
+      fr_units += (int64_t)hkv * FR_SHAPES[q.frs].waves;
     } else {
       q.mode = Mode::BIG;
       q.nrb = (q.pr + FR_ROWS - 1) / FR_ROWS;
@@ -169,7 +182,8 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
   }
   for (Seq& q : v) {
     if (q.mode == Mode::FR) {
-      const int64_t want = std::max<int64_t>(1, ceil_div(NUM_CU, fr_units));
+      // about 8 waves per compute unit over the batch's few-rows workgroups
+      const int64_t want = std::max<int64_t>(1, ceil_div(8 * NUM_CU, fr_units));
       int64_t nc = std::max<int64_t>(1, std::min<int64_t>(want, ceil_div(q.n, FR_MIN_CHUNK)));
       nc = std::max(nc, ceil_div(q.n * krow, SPAN_BYTES));
       q.kc = round32((int)ceil_div(q.n, nc));
@@ -200,7 +214,9 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
 }
 
 // Pass-1 packed-row pitch of a sequence's partials (per KV head).
-int partial_rows(const Seq& q) { return q.mode == Mode::WIDE ? q.rg * WGROWS1 : q.nrb * FR_ROWS; }
+int partial_rows(const Seq& q) {
+  return q.mode == Mode::WIDE ? q.rg * WGROWS1 : q.nrb * FR_SHAPES[q.frs].rows;
+}
 
 // Partial (float2) slots pass 1 needs for sequences [lo, hi).
 int64_t partial_slots(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
@@ -270,22 +286,32 @@ void launch_colsum(const ColsumArgs& args, int items, hipStream_t st) {
   hipLaunchKernelGGL((colsum_kernel<T, D, SW2>), dim3(items), dim3(NTHREADS), 0, st, args);
 }
 
-constexpr int FRW = 8;  // few-rows waves per workgroup
-constexpr int FRT = FR_ROWS / (FRW * TILE);
-
-template <bool PASS2, typename T, int D>
+template <bool PASS2, typename T, int D, int W, int TW>
 void launch_fr(const FrArgs& args, int items, hipStream_t st) {
-  hipLaunchKernelGGL((few_rows_kernel<T, D, PASS2, FRW, FRT>), dim3(items), dim3(FRW * WAVE), 0, st,
-                     args);
+  hipLaunchKernelGGL((few_rows_kernel<T, D, PASS2, W, TW>), dim3(items), dim3(W * WAVE), 0, st, args);
+}
+
+template <bool PASS2, int W, int TW>
+void dispatch_fr_shape(const waits_shape* s, const FrArgs& args, int items, hipStream_t st) {
+  if (s->dtype == WAITS_BF16) {
+    if (s->head_dim == 64) launch_fr<PASS2, bf16_t, 64, W, TW>(args, items, st);
+    else launch_fr<PASS2, bf16_t, 128, W, TW>(args, items, st);
+  } else {
+    launch_fr<PASS2, float, 64, W, TW>(args, items, st);  // fp32 only at head_dim 64 (see plan_seqs)
+  }
 }
 
 template <bool PASS2>
-void dispatch_fr(const waits_shape* s, const FrArgs& args, int items, hipStream_t st) {
-  if (s->dtype == WAITS_BF16) {
-    if (s->head_dim == 64) launch_fr<PASS2, bf16_t, 64>(args, items, st);
-    else launch_fr<PASS2, bf16_t, 128>(args, items, st);
-  } else {
-    launch_fr<PASS2, float, 64>(args, items, st);  // fp32 only at head_dim 64 (see plan_seqs)
+void dispatch_fr(const waits_shape* s, const FrArgs& args, int items, int shape, hipStream_t st) {
+  static_assert(FR_SHAPES[0].waves == 2 && FR_SHAPES[0].tiles == 1, "shape table");
+  static_assert(FR_SHAPES[1].waves == 4 && FR_SHAPES[1].tiles == 1, "shape table");
+  static_assert(FR_SHAPES[2].waves == 8 && FR_SHAPES[2].tiles == 1, "shape table");
+  static_assert(FR_SHAPES[3].waves == 8 && FR_SHAPES[3].tiles == 2, "shape table");
+  switch (shape) {
+    case 0: dispatch_fr_shape<PASS2, 2, 1>(s, args, items, st); break;
+    case 1: dispatch_fr_shape<PASS2, 4, 1>(s, args, items, st); break;
+    case 2: dispatch_fr_shape<PASS2, 8, 1>(s, args, items, st); break;
+    default: dispatch_fr_shape<PASS2, 8, 2>(s, args, items, st); break;
   }
 }
 
@@ -314,20 +340,23 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     SeqTable tab;
     fill_table(tab, v, lo, hi, hkv);
 
-    // few-rows sequences
-    FrArgs f = fr_args(s, q, k);
-    f.lse = lse;
-    f.part = static_cast<float2*>(ws);
-    f.tab = tab;
-    int fr_items = 0;
-    for (int i = lo; i < hi; ++i) {
-      f.tab.first[i - lo] = fr_items;
-      if (v[i].mode == Mode::FR || v[i].mode == Mode::BIG) fr_items += hkv * v[i].nrb * v[i].nc;
-    }
-    f.tab.first[hi - lo] = fr_items;
-    if (fr_items > 0) {
-      dispatch_fr<false>(s, f, fr_items, stream);
-      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    // few-rows kernel: one launch per workgroup shape
+    for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+      FrArgs f = fr_args(s, q, k);
+      f.lse = lse;
+      f.part = static_cast<float2*>(ws);
+      f.tab = tab;
+      int fr_items = 0;
+      for (int i = lo; i < hi; ++i) {
+        f.tab.first[i - lo] = fr_items;
+        if ((v[i].mode == Mode::FR || v[i].mode == Mode::BIG) && v[i].frs == shape)
+          fr_items += hkv * v[i].nrb * v[i].nc;
+      }
+      f.tab.first[hi - lo] = fr_items;
+      if (fr_items > 0) {
+        dispatch_fr<false>(s, f, fr_items, shape, stream);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+      }
     }
 
     // fp32 rows of head_dim 128
@@ -362,17 +391,22 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     cargs.G = G;
     cargs.hkv = hkv;
     cargs.tab = tab;
-    int rows = 0;
+    int rows = 0, max_nc = 1;
     for (int i = lo; i < hi; ++i) {
       cargs.tab.first[i - lo] = rows;
       if (v[i].nc > 1) rows += hkv * v[i].pr;
+      max_nc = std::max(max_nc, v[i].nc);
       // the few-rows kernel writes every (row, chunk) partial; the lse kernel
       // only the chunks a row reaches
       if (v[i].mode != Mode::WIDE) cargs.tab.kc[i - lo] = 0;
     }
     cargs.tab.first[hi - lo] = rows;
     if (rows > 0) {
-      hipLaunchKernelGGL(lse_combine_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, cargs);
+      cargs.team = 1;
+      while (cargs.team < 64 && cargs.team < max_nc / 2) cargs.team *= 2;
+      const int64_t threads = (int64_t)rows * cargs.team;
+      hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         stream, cargs);
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
     }
   }
@@ -394,20 +428,22 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
     SeqTable tab;
     fill_table(tab, v, lo, hi, hkv);
 
-    // few-rows sequences
-    FrArgs f = fr_args(s, q, k);
-    f.lse = const_cast<float*>(lse);
-    f.scores = scores;
-    f.tab = tab;
-    int fr_items = 0;
-    for (int i = lo; i < hi; ++i) {
-      f.tab.first[i - lo] = fr_items;
-      if (v[i].mode == Mode::FR) fr_items += hkv * v[i].nc;
-    }
-    f.tab.first[hi - lo] = fr_items;
-    if (fr_items > 0) {
-      dispatch_fr<true>(s, f, fr_items, stream);
-      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    // few-rows sequences: one launch per workgroup shape
+    for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+      FrArgs f = fr_args(s, q, k);
+      f.lse = const_cast<float*>(lse);
+      f.scores = scores;
+      f.tab = tab;
+      int fr_items = 0;
+      for (int i = lo; i < hi; ++i) {
+        f.tab.first[i - lo] = fr_items;
+        if (v[i].mode == Mode::FR && v[i].frs == shape) fr_items += hkv * v[i].nc;
+      }
+      f.tab.first[hi - lo] = fr_items;
+      if (fr_items > 0) {
+        dispatch_fr<true>(s, f, fr_items, shape, stream);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+      }
     }
 
     // key blocks of the longer sequences

@@ -52,6 +52,12 @@ def workload(name: str):
         return dict(desc="Llama-3.1-8B layer shape, one layer N=131072, a=1 b=16, budget 2048",
                     hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[1.0], b=[16],
                     budget=2048, layers=1)
+    if name in ("long_snap", "long_tova"):
+        b = 16 if name == "long_snap" else 1
+        return dict(desc=f"Llama-3.1-8B layer shape, one layer N=131072, a=inf b={b} "
+                         f"({'SnapKV' if b > 1 else 'TOVA'} limit), budget 2048",
+                    hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[math.inf], b=[b],
+                    budget=2048, layers=1)
     if name == "mistral":
         rng = np.random.default_rng(3)
         lengths = [int(x) for x in rng.integers(8192, 32768, endpoint=True, size=8)]
@@ -74,16 +80,20 @@ def live_rows_fp32(n: int, a: float, b: int) -> np.ndarray:
 
 
 def algorithmic_work(wl):
-    """Per-launch algorithmic flops of one QK^T pass and bytes of select/compact."""
-    flops_pass = 0.0
+    """Per-launch algorithmic flops and bytes of one QK^T pass, and bytes of
+    select/compact.  Pass bytes: K read once, the live Q rows, lse (pass 1
+    writes it, pass 2 reads it); pass 2 also writes the scores."""
+    flops_pass, live = 0.0, 0
     for n, a, b in zip(wl["lengths"], wl["a"], wl["b"]):
         rows = live_rows_fp32(n, a, b)
         flops_pass += 2.0 * wl["d"] * wl["hq"] * float(np.sum(rows + 1))
-    hkv, d, budget, B = wl["hkv"], wl["d"], wl["budget"], len(wl["lengths"])
+        live += len(rows)
+    hkv, hq, d, budget, B = wl["hkv"], wl["hq"], wl["d"], wl["budget"], len(wl["lengths"])
     T = sum(wl["lengths"])
+    bytes_pass = hkv * T * d * 2 + hq * live * d * 2 + hq * live * 4
     select_bytes = hkv * T * 4 + B * hkv * budget * 4
     compact_bytes = 2 * 2 * B * hkv * budget * d * 2 + B * hkv * budget * 4
-    return flops_pass, select_bytes, compact_bytes
+    return flops_pass, bytes_pass, select_bytes, compact_bytes
 
 
 def make_inputs(wl, device):
@@ -278,7 +288,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b", choices=["8b", "1b", "long", "mistral"])
+    ap.add_argument("--workload", default="8b",
+                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -347,7 +358,7 @@ def main():
     per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            for j, nm in enumerate(names)}  # ms per launch (pass 1 includes its combine, if any)
 
-    flops_pass, sel_bytes, cmp_bytes = algorithmic_work(wl)
+    flops_pass, bytes_pass, sel_bytes, cmp_bytes = algorithmic_work(wl)
     tokens_layers = float(sum(wl["lengths"]))  # every sequence is one layer of one prompt
     value = tokens_layers / (ms_step * 1e-3)
 
@@ -357,7 +368,18 @@ def main():
         "select_compact": (sel_bytes + cmp_bytes) / (per["select_compact"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     dom = max(("pass1_lse", "pass2_colsum"), key=lambda nm: per[nm])
-    achieved = flops_pass / (per[dom] * 1e-3) / 1e12
+    # the passes are MFMA-bound above the ridge (peak flops / peak bytes), HBM-bound below
+    mfma_bound = flops_pass / bytes_pass >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "kernel": dom,
+                "achieved": flops_pass / (per[dom] * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "kernel": dom,
+                "achieved": bytes_pass / (per[dom] * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(dom, args.workload)
     passes_ms = per["pass1_lse"] + per["pass2_colsum"]
     sc_ms = per["select_compact"]
 
@@ -377,15 +399,13 @@ def main():
         "config": {"workload": wl["desc"], "sequences": B, "tokens_per_step": T,
                    "q_heads": hq, "kv_heads": hkv, "head_dim": d, "select_budget": budget,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(dom, args.workload)},
+        "roofline": roof,
         "passes_mfma_frac": 2 * flops_pass / (passes_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "select_compact_hbm_frac": (sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels_us": {nm: per[nm] * 1e3 for nm in names},
         "kernel_frac": frac,
-        "algorithmic": {"flops_per_pass": flops_pass, "select_bytes": sel_bytes,
+        "algorithmic": {"flops_per_pass": flops_pass, "bytes_per_pass": bytes_pass,
+                        "select_bytes": sel_bytes,
                         "compact_bytes": cmp_bytes},
         "input_gen_s": t_gen,
         "host": platform.node(),
