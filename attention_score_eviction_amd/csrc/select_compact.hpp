@@ -44,6 +44,7 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int SEL_SUB = 32;          // sub-counters per digit
 constexpr int SEL_FUSE_MAX = 8192;   // largest budget the fused gather keeps in LDS
+constexpr int SEL_BATCH = 16;        // keys per lane loaded together (no register cache)
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -120,21 +121,37 @@ select_kernel(const SelectArgs args) {
     static_assert(SEL_THREADS == 4 * 256, "one histogram word per thread");
     __syncthreads();
 
-    // f(i, valid, bits) over this lane's keys, in position order; with a
-    // register cache, `live` (bit i: some lane of the wave still matches the
-    // prefix with its i-th key) skips keys no lane needs.
-    uint32_t live = ~0u;
+    // f(i, valid, bits) over this lane's keys, in position order.  `live`
+    // (wave-uniform) skips keys no lane still needs: bit i stands for the
+    // lane's i-th key with a register cache, for its i-th group of SEL_BATCH
+    // keys without one (all bits set past 64 groups).  Without a cache the
+    // keys are loaded SEL_BATCH at a time, all loads in flight together.
+    uint64_t live = ~0ull;
     auto each_key = [&](auto&& f) {
       if constexpr (PTC > 0) {
 #pragma unroll
         for (int i = 0; i < PTC; ++i)
           if (i < iters && ((live >> i) & 1u)) f(i, e0 + i * WAVE < N, cache[i]);  // wave-uniform
       } else {
-        for (int i = 0; i < iters; ++i) {
-          const int e = e0 + i * WAVE;
-          f(i, e < N, e < N ? s[e] : 0u);
+        for (int i0 = 0; i0 < iters; i0 += SEL_BATCH) {
+          const int grp = i0 / SEL_BATCH;
+          if (grp < 64 && !((live >> grp) & 1u)) continue;  // wave-uniform
+          uint32_t c[SEL_BATCH];
+#pragma unroll
+          for (int i = 0; i < SEL_BATCH; ++i) {
+            const int e = e0 + (i0 + i) * WAVE;
+            c[i] = (i0 + i < iters && e < N) ? s[e] : 0u;
+          }
+#pragma unroll
+          for (int i = 0; i < SEL_BATCH; ++i)
+            if (i0 + i < iters) f(i0 + i, e0 + (i0 + i) * WAVE < N, c[i]);
         }
       }
+    };
+    // the `live` bit of the lane's i-th key
+    auto live_bit = [&](int i) -> uint64_t {
+      const int b = PTC > 0 ? i : i / SEL_BATCH;
+      return b < 64 ? 1ull << b : 0ull;
     };
 
     // pass 1 (top digit, shared by almost every key): per-(digit, lane % 32)
@@ -162,14 +179,14 @@ select_kernel(const SelectArgs args) {
 #pragma unroll
     for (int pass = 1; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      uint32_t nlive = 0;
+      uint64_t nlive = iters > 64 * SEL_BATCH && PTC == 0 ? ~0ull : 0ull;
       each_key([&](int i, bool ok, uint32_t u) {
         const bool take = ok && (u & pmask) == prefix;
         const uint64_t m = __ballot(take);
-        nlive |= (m != 0 ? 1u : 0u) << i;
+        if (m != 0) nlive |= live_bit(i);
         if (take) atomicAdd(&hist[pass][(u >> shift) & 255u], 1);
       });
-      if constexpr (PTC > 0) live = nlive;
+      live = nlive;
       __syncthreads();
       pick_digit(hist[pass], krem, lane, dgt, above);
       krem -= above;
@@ -178,7 +195,7 @@ select_kernel(const SelectArgs args) {
     }
     const uint32_t thr = prefix;
     const int need_eq = krem;  // keys equal to thr that are kept (lowest positions)
-    live = ~0u;
+    live = ~0ull;
 
     int n_gt = 0, n_eq = 0;  // wave totals (uniform)
     each_key([&](int, bool ok, uint32_t u) {

@@ -16,6 +16,7 @@
 #include "few_rows.hpp"
 #include "key_blocks.hpp"
 #include "select_compact.hpp"
+#include "select_wide.hpp"
 
 namespace waits {
 namespace {
@@ -34,6 +35,7 @@ constexpr int BIG_MIN_CHUNK = 1024;               // row blocks: shortest pass-1
 constexpr int KB_MIN_ROWS = 256;                  // key blocks: fewest rows per chunk
 constexpr int KB_MAX_CHUNKS = 64;                 // key blocks: most row chunks
 constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chunk (< 2^31)
+constexpr int SEL_WIDE_MIN = SEL_THREADS * 32;    // longer key ranges: select over several workgroups
 
 // Few-rows workgroup shapes: a head takes the smallest that holds its packed
 // rows (row blocks of longer heads use the largest).
@@ -520,14 +522,21 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
   return WAITS_OK;
 }
 
-int check_select(const waits_shape* s, const float* scores, int32_t budget, const int32_t* idx) {
+// The fields waits_select reads: batch, cu_seqlens, n_kv_heads; and the budget.
+int check_select_shape(const waits_shape* s, int32_t budget) {
   if (!s || !s->cu_seqlens || s->batch < 1 || s->n_kv_heads < 1 || s->cu_seqlens[0] != 0)
     return WAITS_EINVAL;
   for (int i = 0; i < s->batch; ++i) {
     const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
     if (n < 0 || n > MAX_SEQ_LEN) return WAITS_EINVAL;
   }
-  if (budget < 1 || !idx || !is_aligned(idx, 4)) return WAITS_EINVAL;
+  return budget < 1 ? WAITS_EINVAL : WAITS_OK;
+}
+
+int check_select(const waits_shape* s, const float* scores, int32_t budget, const int32_t* idx) {
+  const int rc = check_select_shape(s, budget);
+  if (rc != WAITS_OK) return rc;
+  if (!idx || !is_aligned(idx, 4)) return WAITS_EINVAL;
   if (s->cu_seqlens[s->batch] > 0 && (!scores || !is_aligned(scores, 4))) return WAITS_EINVAL;
   return WAITS_OK;
 }
@@ -542,15 +551,89 @@ int check_gather(const waits_shape* s, const void* k, const void* v, const int32
   return WAITS_OK;
 }
 
+// Workspace of the several-workgroup select for sequences [lo, hi): the
+// per-(sequence, head) digit histograms, then one (above, equal) count pair
+// per chunk.  0 when every sequence is short enough for one workgroup.
+struct WideWs {
+  size_t hist_bytes = 0, count_bytes = 0;
+  int items = 0;
+};
+WideWs wide_ws(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
+  WideWs w;
+  int gmax = 0;
+  for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+  if (gmax <= SEL_WIDE_MIN) return w;
+  for (int i = lo; i < hi; ++i) w.items += s->n_kv_heads * wide_chunks(v[i].n);
+  w.hist_bytes = (size_t)(hi - lo) * s->n_kv_heads * 4 * 256 * sizeof(int);
+  w.count_bytes = (size_t)w.items * sizeof(int2);
+  return w;
+}
+
+size_t select_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+  size_t mx = 0;
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const WideWs w = wide_ws(s, v, lo, std::min(s->batch, lo + MAXB));
+    mx = std::max(mx, w.hist_bytes + w.count_bytes);
+  }
+  return mx;
+}
+
 template <bool FUSE>
 int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
-               const void* k, const void* vv, void* k_out, void* v_out, hipStream_t stream) {
+               const void* k, const void* vv, void* k_out, void* v_out, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, nullptr, nullptr);
+  const size_t need = select_ws_bytes(s, v);
+  if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 16)))) return WAITS_EWORKSPACE;
   const int e = FUSE ? elt_bytes(s->dtype) : 0;
   const int row_bytes = FUSE ? s->head_dim * e : 0;
   for (int lo = 0; lo < s->batch; lo += MAXB) {
     const int hi = std::min(s->batch, lo + MAXB);
     const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
+    int gmax = 0;
+    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+    if (gmax > SEL_WIDE_MIN) {
+      const WideWs w = wide_ws(s, v, lo, hi);
+      WideArgs args;
+      std::memset(&args, 0, sizeof(args));
+      args.scores = scores;
+      args.idx = idx + first_row;
+      args.hist = static_cast<int*>(ws);
+      args.counts = reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.hist_bytes);
+      args.T = s->cu_seqlens[s->batch];
+      args.hkv = s->n_kv_heads;
+      args.budget = budget;
+      args.k = static_cast<const unsigned char*>(k);
+      args.v = static_cast<const unsigned char*>(vv);
+      args.k_out = FUSE ? static_cast<unsigned char*>(k_out) + first_row * row_bytes : nullptr;
+      args.v_out = FUSE ? static_cast<unsigned char*>(v_out) + first_row * row_bytes : nullptr;
+      args.st = strides_of(s);
+      args.elt = e;
+      args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
+      fill_table(args.tab, v, lo, hi, s->n_kv_heads);
+      int items = 0;
+      for (int i = lo; i < hi; ++i) {
+        args.tab.first[i - lo] = items;
+        items += s->n_kv_heads * wide_chunks(v[i].n);
+      }
+      args.tab.first[hi - lo] = items;
+      const int64_t words = (int64_t)(w.hist_bytes / sizeof(int));
+      hipLaunchKernelGGL(wide_zero_kernel, dim3((unsigned)std::min<int64_t>(1024, (words + 255) / 256)),
+                         dim3(256), 0, stream, args.hist, words);
+      if (launched() != WAITS_OK) return WAITS_EDEVICE;
+      if (items > 0) {
+        for (int d = 0; d < 4; ++d) {
+          args.digit = d;
+          hipLaunchKernelGGL(wide_hist_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
+          if (launched() != WAITS_OK) return WAITS_EDEVICE;
+        }
+        hipLaunchKernelGGL(wide_count_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+        hipLaunchKernelGGL((wide_emit_kernel<FUSE>), dim3(items), dim3(SEL_THREADS), 0, stream, args);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+      }
+      continue;
+    }
     SelectArgs args;
     args.scores = scores;
     args.idx = idx + first_row;
@@ -565,8 +648,6 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     args.elt = e;
     args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
     fill_table(args.tab, v, lo, hi, s->n_kv_heads);
-    int gmax = 0;
-    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
     const dim3 grid((hi - lo) * s->n_kv_heads);
     if (gmax <= SEL_THREADS * 16)
       hipLaunchKernelGGL((select_kernel<16, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
@@ -702,11 +783,20 @@ int waits_score(const waits_shape* s, const void* q, const void* k, const float*
   return run_colsum(s, q, k, lse, a, b, scores, part, ws_bytes - lse_bytes, stream);
 }
 
+int waits_select_workspace_bytes(const waits_shape* s, int32_t budget, size_t* bytes) {
+  const int rc = check_select_shape(s, budget);
+  if (rc != WAITS_OK) return rc;
+  if (!bytes) return WAITS_EINVAL;
+  *bytes = select_ws_bytes(s, plan_seqs(s, nullptr, nullptr));
+  return WAITS_OK;
+}
+
 int waits_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
-                 hipStream_t stream) {
+                 void* ws, size_t ws_bytes, hipStream_t stream) {
   const int rc = check_select(s, scores, budget, idx);
   if (rc != WAITS_OK) return rc;
-  return run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, stream);
+  return run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, ws,
+                           ws_bytes, stream);
 }
 
 int waits_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
@@ -718,18 +808,19 @@ int waits_compact(const waits_shape* s, const void* k, const void* v, const int3
 }
 
 int waits_select_compact(const waits_shape* s, const float* scores, const void* k, const void* v,
-                         int32_t budget, int32_t* idx, void* k_out, void* v_out,
-                         hipStream_t stream) {
+                         int32_t budget, int32_t* idx, void* k_out, void* v_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(s, false);
   if (rc == WAITS_OK) rc = check_select(s, scores, budget, idx);
   if (rc == WAITS_OK) rc = check_gather(s, k, v, idx, budget, k_out, v_out);
   if (rc != WAITS_OK) return rc;
   if (budget > SEL_FUSE_MAX) {
-    rc = run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, stream);
+    rc = run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes,
+                           stream);
     if (rc != WAITS_OK) return rc;
     return run_compact(s, k, v, idx, budget, k_out, v_out, stream);
   }
-  return run_select<true>(s, scores, budget, idx, k, v, k_out, v_out, stream);
+  return run_select<true>(s, scores, budget, idx, k, v, k_out, v_out, ws, ws_bytes, stream);
 }
 
 const char* waits_strerror(int code) {

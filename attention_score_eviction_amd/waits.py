@@ -64,9 +64,10 @@ _SIGS = {
     "waits_colsum_workspace_bytes": [_SP, _FP, _IP, ctypes.POINTER(ctypes.c_size_t)],
     "waits_colsum": [_SP, _P, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
     "waits_score": [_SP, _P, _P, _FP, _IP, _P, _P, ctypes.c_size_t, _P],
-    "waits_select": [_SP, _P, ctypes.c_int32, _P, _P],
+    "waits_select": [_SP, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
+    "waits_select_workspace_bytes": [_SP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
-    "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P],
+    "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 
@@ -264,22 +265,37 @@ def score(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
     return out
 
 
-def select(scores: torch.Tensor, cu_seqlens, budget: int,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Top-``budget`` key positions per (sequence, KV head), ascending, -1 padded."""
-    cu = np.asarray(cu_seqlens, dtype=np.int64)
-    hkv = scores.shape[0]
-    if out is None:
-        out = torch.empty((len(cu) - 1, hkv, int(budget)), dtype=torch.int32,
-                          device=scores.device)
+def _select_shape(cu_seqlens, hkv: int):
+    cu_c = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
     shape = WaitsShape()
-    cu_c = np.ascontiguousarray(cu)
     shape.batch = len(cu_c) - 1
     shape.cu_seqlens = cu_c.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     shape.n_kv_heads = hkv
     shape.n_q_heads = hkv
+    return shape, cu_c
+
+
+def select_workspace_bytes(cu_seqlens, hkv: int, budget: int) -> int:
+    shape, _keep = _select_shape(cu_seqlens, hkv)
+    out = ctypes.c_size_t(0)
+    _check("waits_select_workspace_bytes",
+           lib().waits_select_workspace_bytes(ctypes.byref(shape), int(budget), ctypes.byref(out)))
+    return out.value
+
+
+def select(scores: torch.Tensor, cu_seqlens, budget: int,
+           out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-``budget`` key positions per (sequence, KV head), ascending, -1 padded."""
+    hkv = scores.shape[0]
+    shape, cu_c = _select_shape(cu_seqlens, hkv)
+    if out is None:
+        out = torch.empty((len(cu_c) - 1, hkv, int(budget)), dtype=torch.int32,
+                          device=scores.device)
+    ws = _workspace(select_workspace_bytes(cu_c, hkv, budget), scores.device, workspace)
     _check("waits_select", lib().waits_select(
-        ctypes.byref(shape), _ptr(scores), int(budget), _ptr(out), _stream(scores)))
+        ctypes.byref(shape), _ptr(scores), int(budget), _ptr(out), _ptr(ws),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(scores)))
     return out
 
 
@@ -302,7 +318,8 @@ def compact(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, cu_seqlens, bud
 
 def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
                    budget: int, idx: Optional[torch.Tensor] = None,
-                   k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None):
+                   k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
     """select() then compact() in one launch: (idx, k_out, v_out)."""
     _last_dim_contiguous(k, v)
     if k.stride() != v.stride():
@@ -317,8 +334,10 @@ def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_se
         k_out = torch.empty((nb, hkv, int(budget), d), dtype=k.dtype, device=k.device)
     if v_out is None:
         v_out = torch.empty((nb, hkv, int(budget), d), dtype=v.dtype, device=v.device)
+    ws = _workspace(select_workspace_bytes(m.cu, hkv, budget), k.device, workspace)
     _check("waits_select_compact", lib().waits_select_compact(
         m.sp, _ptr(scores), _ptr(k), _ptr(v), int(budget), _ptr(idx), _ptr(k_out), _ptr(v_out),
+        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
         _stream(k)))
     return idx, k_out, v_out
 

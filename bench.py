@@ -330,6 +330,8 @@ def main():
     scores = torch.empty((hkv, T), dtype=torch.float32, device=dev)
     idx = torch.empty((B, hkv, budget), dtype=torch.int32, device=dev)
     kc = torch.empty((B, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    sel_ws = torch.empty(max(W.waits.select_workspace_bytes(cu, hkv, budget), 256),
+                         dtype=torch.uint8, device=dev)
     vc = torch.empty_like(kc)
 
     stream = torch.cuda.current_stream(dev)
@@ -341,7 +343,7 @@ def main():
         if e: e[1].record(stream)
         W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws)
         if e: e[2].record(stream)
-        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc)  # one launch
+        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws)
         if e: e[3].record(stream)
 
     for _ in range(args.warmup):

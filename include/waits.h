@@ -150,7 +150,17 @@ int waits_score(const waits_shape* shape, const void* q, const void* k,
  * n_kv_heads are read from `shape`.
  */
 int waits_select(const waits_shape* shape, const float* scores,
-                 int32_t select_budget, int32_t* idx, hipStream_t stream);
+                 int32_t select_budget, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace waits_select and waits_select_compact need for
+ * this batch: 0 unless a sequence has more than 32768 keys, whose selection
+ * is split over several workgroups that meet in the workspace (per-head digit
+ * histograms and per-chunk counts).  workspace: device, 16-byte aligned.
+ */
+int waits_select_workspace_bytes(const waits_shape* shape, int32_t select_budget,
+                                 size_t* bytes);
 
 /*
  * Compaction (README introduction: the retained key-value pairs): copies
@@ -166,18 +176,18 @@ int waits_compact(const waits_shape* shape, const void* k, const void* v,
                   void* v_out, hipStream_t stream);
 
 /*
- * Selection and compaction in one launch: the outputs of waits_select
- * (idx) followed by waits_compact (k_out, v_out), with the same arguments,
+ * Selection and compaction fused: the outputs of waits_select (idx)
+ * followed by waits_compact (k_out, v_out), with the same arguments,
  * layouts and error codes as those two calls, bit for bit.  The workgroup
- * that selects a (sequence, KV head) gathers its rows while the positions
- * are still in LDS, so the gather needs no second launch and no re-read of
- * idx.  For select_budget > 8192 it runs the two kernels one after the
- * other on `stream`.
+ * that places a key also copies its K/V rows while the position is at hand,
+ * so the gather needs no launch of its own and no re-read of idx.  For
+ * select_budget > 8192 it runs the select and compact kernels one after
+ * the other on `stream`.  workspace: as for waits_select.
  */
 int waits_select_compact(const waits_shape* shape, const float* scores,
                          const void* k, const void* v, int32_t select_budget,
-                         int32_t* idx, void* k_out, void* v_out,
-                         hipStream_t stream);
+                         int32_t* idx, void* k_out, void* v_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a WAITS_E* code. */
 const char* waits_strerror(int code);

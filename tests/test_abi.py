@@ -114,9 +114,10 @@ def test_null_pointers_and_workspace():
 def test_select_and_compact_validation():
     s = _shape()
     lib = W.lib()
-    assert lib.waits_select(ctypes.byref(s), FAKE, 0, FAKE, None) == W.WAITS_EINVAL
-    assert lib.waits_select(ctypes.byref(s), FAKE, 128, None, None) == W.WAITS_EINVAL
-    assert lib.waits_select(ctypes.byref(_shape(cu=[0, -1])), FAKE, 8, FAKE, None) == W.WAITS_EINVAL
+    assert lib.waits_select(ctypes.byref(s), FAKE, 0, FAKE, None, 0, None) == W.WAITS_EINVAL
+    assert lib.waits_select(ctypes.byref(s), FAKE, 128, None, None, 0, None) == W.WAITS_EINVAL
+    assert lib.waits_select(ctypes.byref(_shape(cu=[0, -1])), FAKE, 8, FAKE, None, 0,
+                            None) == W.WAITS_EINVAL
     assert lib.waits_compact(ctypes.byref(s), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == W.WAITS_EINVAL
     assert lib.waits_compact(ctypes.byref(s), FAKE, FAKE, FAKE, 8, None, FAKE, None) == W.WAITS_EINVAL
     bad = _shape(d=80)
@@ -167,6 +168,20 @@ def test_workspace_sizes():
     assert lse_ws > 0 and col_ws > 0 and col_ws % (8 * 4096 * 4) == 0
     assert (W.score_workspace_bytes(q, k, [0, 4096], [0.0], [1])
             >= 32 * 4096 * 4 + max(lse_ws, col_ws))
+
+
+def test_select_workspace():
+    # one workgroup per (sequence, head) up to 32768 keys: no workspace
+    assert W.select_workspace_bytes([0, 32768], 8, 128) == 0
+    assert W.select_workspace_bytes([0, 0], 8, 128) == 0
+    # longer: 4096-key chunks; histograms [seq, head, 4, 256] int32 + a count pair per chunk
+    need = W.select_workspace_bytes([0, 131072, 131072 + 5000], 8, 2048)
+    assert need == 2 * 8 * 4 * 256 * 4 + 8 * (32 + 2) * 8
+    s = _shape(cu=[0, 40000], hkv=2)
+    lib = W.lib()
+    assert lib.waits_select(ctypes.byref(s), FAKE, 64, FAKE, None, 0, None) == W.WAITS_EWORKSPACE
+    assert lib.waits_select(ctypes.byref(s), FAKE, 64, FAKE, ctypes.c_void_p(0x100008), 1 << 20,
+                            None) == W.WAITS_EWORKSPACE   # not 16-byte aligned
 
 
 def test_colsum_workspace_validation():
