@@ -14,6 +14,7 @@
 #include "pass1_lse.hpp"
 #include "pass2_colsum.hpp"
 #include "few_rows.hpp"
+#include "few_rows16.hpp"
 #include "key_blocks.hpp"
 #include "select_compact.hpp"
 #include "select_wide.hpp"
@@ -38,12 +39,18 @@ constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chu
 constexpr int SEL_WIDE_MIN = SEL_THREADS * 32;    // longer key ranges: select over several workgroups
 
 // Few-rows workgroup shapes: a head takes the smallest that holds its packed
-// rows (row blocks of longer heads use the largest).
+// rows (row blocks of longer heads use the largest).  tiles: 32-row tiles per
+// wave; t16: 16-row tiles per wave of the 16x16 MFMA kernel (bf16 heads of one
+// row block only), which pads rows to 16 rather than to 256.  Its tiles cost
+// more per row than 32-row tiles (twice the MFMA operand reads per flop), so
+// it takes a head only while the busiest SIMD runs fewer rows than the
+// 512-row shape gives it: at most 7 16-row tiles per SIMD, 448 rows.
 struct FrShape {
-  int rows, waves, tiles;
+  int rows, waves, tiles, t16;
 };
-constexpr FrShape FR_SHAPES[] = {{64, 2, 1}, {128, 4, 1}, {256, 8, 1}, {512, 8, 2}};
-constexpr int FR_NSHAPES = 4;
+constexpr FrShape FR_SHAPES[] = {{64, 2, 1, 0},  {128, 4, 1, 0}, {256, 8, 1, 0},
+                                 {384, 8, 0, 3}, {448, 8, 0, 4}, {512, 8, 2, 0}};
+constexpr int FR_NSHAPES = 6;
 constexpr int FR_BIG_SHAPE = FR_NSHAPES - 1;
 static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the largest shape");
 
@@ -172,7 +179,8 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       q.mode = Mode::FR;
       q.nrb = 1;
       q.frs = 0;
-      while (FR_SHAPES[q.frs].rows < q.pr) ++q.frs;
+      while (FR_SHAPES[q.frs].rows < q.pr || (FR_SHAPES[q.frs].t16 > 0 && s->dtype != WAITS_BF16))
+        ++q.frs;
       fr_units += (int64_t)hkv * FR_SHAPES[q.frs].waves;
     } else {
       q.mode = Mode::BIG;
@@ -303,16 +311,31 @@ void dispatch_fr_shape(const waits_shape* s, const FrArgs& args, int items, hipS
   }
 }
 
+template <bool PASS2, int NT>
+void dispatch_fr16(const waits_shape* s, const FrArgs& args, int items, hipStream_t st) {
+  if (s->head_dim == 64)
+    hipLaunchKernelGGL((few_rows16_kernel<64, PASS2, NT>), dim3(items), dim3(8 * WAVE), 0, st, args);
+  else
+    hipLaunchKernelGGL((few_rows16_kernel<128, PASS2, NT>), dim3(items), dim3(8 * WAVE), 0, st, args);
+}
+
 template <bool PASS2>
 void dispatch_fr(const waits_shape* s, const FrArgs& args, int items, int shape, hipStream_t st) {
   static_assert(FR_SHAPES[0].waves == 2 && FR_SHAPES[0].tiles == 1, "shape table");
   static_assert(FR_SHAPES[1].waves == 4 && FR_SHAPES[1].tiles == 1, "shape table");
   static_assert(FR_SHAPES[2].waves == 8 && FR_SHAPES[2].tiles == 1, "shape table");
-  static_assert(FR_SHAPES[3].waves == 8 && FR_SHAPES[3].tiles == 2, "shape table");
+  static_assert(FR_SHAPES[3].waves == 8 && FR_SHAPES[3].t16 == 3 && FR_SHAPES[3].rows == 8 * 3 * 16,
+                "shape table");
+  static_assert(FR_SHAPES[4].waves == 8 && FR_SHAPES[4].t16 == 4 && FR_SHAPES[4].rows > 8 * 3 * 16 &&
+                    FR_SHAPES[4].rows <= 8 * 4 * 16,
+                "shape table");
+  static_assert(FR_SHAPES[5].waves == 8 && FR_SHAPES[5].tiles == 2, "shape table");
   switch (shape) {
     case 0: dispatch_fr_shape<PASS2, 2, 1>(s, args, items, st); break;
     case 1: dispatch_fr_shape<PASS2, 4, 1>(s, args, items, st); break;
     case 2: dispatch_fr_shape<PASS2, 8, 1>(s, args, items, st); break;
+    case 3: dispatch_fr16<PASS2, 3>(s, args, items, st); break;
+    case 4: dispatch_fr16<PASS2, 4>(s, args, items, st); break;
     default: dispatch_fr_shape<PASS2, 8, 2>(s, args, items, st); break;
   }
 }

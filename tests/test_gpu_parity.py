@@ -173,6 +173,21 @@ def test_ragged_small_sizes(n, hq, hkv, d):
         _full_check(bt, [a], [b], 64)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("a,b", [(math.inf, 65), (math.inf, 96), (math.inf, 97), (1.0, 16),
+                                 (math.inf, 112), (math.inf, 113), (math.inf, 128)])
+def test_mid_size_heads_split_keys(d, a, b):
+    # G = 4 and a = inf keep the last b rows: 4 b packed rows per KV head, here
+    # 260..512: the 16-row-tile shapes (partly filled and full, up to 448 rows)
+    # and the 32-row shape just past them; a = 1, b = 16 keeps about 105 rows.  N = 6000 cuts each head's keys into chunks
+    # that the combine merges.
+    _say(f"mid-size heads d={d} a={a} b={b}")
+    bt = make_prompt(60 + b + d, 6000, 8, 2, d, heavy=True, dtype="bf16")
+    _full_check(bt, [a], [b], 256)
+    bt = make_batch([70, 71, 72], [700, 6000, 2500], 8, 2, d, heavy=True)
+    _full_check(bt, [a, 0.0, a], [b, 1, b], 256)
+
+
 def test_batch_with_empty_and_tiny_sequences():
     _say("batch with empty sequences")
     bt = make_batch([5, 6, 7, 8, 9], [0, 1, 700, 0, 45], 8, 2, 64, heavy=True)
