@@ -168,15 +168,17 @@ def cpu_baseline(wl, budget_s: float):
 
 
 KERNEL_SOURCES = ("attention_score_eviction_amd/csrc/few_rows.hpp",
+                  "attention_score_eviction_amd/csrc/few_rows16.hpp",
                   "attention_score_eviction_amd/csrc/key_blocks.hpp",
                   "attention_score_eviction_amd/csrc/select_compact.hpp",
                   "attention_score_eviction_amd/csrc/device_common.hpp",
                   "attention_score_eviction_amd/csrc/kernel_args.hpp")
 
 # Bench kernel names and a substring of the device symbol each launches (the
-# timed kernel; pass 1 may add the small combine kernel, which is not counted).
-KERNEL_SYMBOLS = {"pass1_lse": ("few_rows_kernel", "false"),
-                  "pass2_colsum": ("few_rows_kernel", "true"),
+# timed kernel: few_rows_kernel or few_rows16_kernel, by the heads' row count;
+# pass 1 may add the small combine kernel, which is not counted).
+KERNEL_SYMBOLS = {"pass1_lse": ("few_rows", "false"),
+                  "pass2_colsum": ("few_rows", "true"),
                   "select_compact": ("select_kernel", "true")}
 
 
