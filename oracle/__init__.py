@@ -1,4 +1,5 @@
-"""CPU oracle for the WAITS prefill KV-selection path (score -> select -> compact).
+"""CPU oracle for the WAITS prefill KV-selection path (score -> select -> compact)
+and for decode attention over the compacted cache.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in
@@ -8,14 +9,19 @@ shares no code, constants or helpers with them.
 * ``waits_oracle`` -- the plain definition in float64 numpy (library matmul,
   exp and sort as steps; nothing blocked, fused or reordered beyond splitting
   query rows into chunks, which does not change any sum's terms).
-* ``brute`` -- the same definition in scalar pure-Python loops with
-  ``math.fsum``, for tiny inputs only; it pins the numpy oracle.
+* ``decode_oracle`` -- decode attention of one new query per head over the
+  kept cache rows, in float64 numpy.
+* ``brute`` -- the same definitions in scalar pure-Python loops with
+  ``math.fsum``, for tiny inputs only; they pin the numpy oracles.
 
 Pins (see ``tests/test_oracle.py``): closed forms for uniform attention
 (harmonic numbers), the H2O / TOVA / SnapKV limits checked against
 ``scipy.special.softmax``, the attention-mass invariant, causal support
 invariance, GQA head-permutation invariance, brute force on N <= 64, and a
-full lexicographic sort for top-k.  No function here is "parity unpinned".
+full lexicographic sort for top-k; for decode (``tests/test_decode_oracle.py``)
+closed forms (uniform, one and two rows), the prefill oracle's last causal row
+(TOVA limit and lse), brute force, and softmax invariants.  No function here
+is "parity unpinned".
 """
 from .waits_oracle import (  # noqa: F401
     sigmoid_weights,
@@ -27,3 +33,4 @@ from .waits_oracle import (  # noqa: F401
     waits_select,
     waits_compact,
 )
+from .decode_oracle import waits_decode  # noqa: F401

@@ -56,3 +56,21 @@ def topk(s, budget: int):
     ranked = sorted(range(len(s)), key=lambda i: (-s[i], i))
     kept = sorted(ranked[:budget])
     return kept + [-1] * (budget - len(kept))
+
+
+def decode(qv, kc, vc, scale: float):
+    """Decode attention of one query vector ``qv[d]`` over cache rows
+    ``kc[n][d]``, ``vc[n][d]`` (nested lists of floats), written as scalar
+    loops: softmax over the rows of ``scale * <q, k_j>``, then the weighted
+    sum of the ``v_j``.  Returns ``(out[d], lse)``; an empty cache gives
+    zeros and -inf.  (README "Quickstart": generation after init_cache
+    attends over the kept rows.)"""
+    d = len(qv)
+    if not kc:
+        return [0.0] * d, -math.inf
+    logits = [scale * math.fsum(qv[i] * row[i] for i in range(d)) for row in kc]
+    top = max(logits)
+    ex = [math.exp(x - top) for x in logits]
+    z = math.fsum(ex)
+    out = [math.fsum(ex[j] * vc[j][i] for j in range(len(kc))) / z for i in range(d)]
+    return out, top + math.log(z)
