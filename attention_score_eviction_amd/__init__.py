@@ -1,4 +1,5 @@
-"""WAITS prefill KV selection (score -> top-k select -> compact) on AMD MI355X.
+"""WAITS prefill KV selection (score -> top-k select -> compact) on AMD MI355X,
+and decode attention over the compacted cache.
 
 The computation runs in ``libwaits.so`` (hand-written HIP kernels for
 gfx950, C ABI in ``include/waits.h``); ``waits`` is its Python binding.
@@ -8,6 +9,7 @@ from .waits import (  # noqa: F401
     WaitsError,
     colsum,
     compact,
+    decode,
     lse,
     score,
     score_select_compact,

@@ -33,7 +33,7 @@ def compile_command(out: str) -> list:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
-        os.path.join(CSRC, "waits_api.hip"), "-o", out,
+        os.path.join(CSRC, "waits_api.hip"), os.path.join(CSRC, "decode_api.hip"), "-o", out,
     ]
 
 

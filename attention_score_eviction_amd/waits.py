@@ -9,6 +9,9 @@ Layouts (token-major packed batch, positions restart per sequence):
   q [T, Hq, d], k / v [T, Hkv, d]  (any strides with d contiguous)
   lse [Hq, T] fp32, scores [Hkv, T] fp32
   idx [B, Hkv, budget] int32, k_out / v_out [B, Hkv, budget, d]
+Decode over the compacted cache (dense):
+  q [B, Hq, d], k_cache / v_cache [B, Hkv, capacity, d], lens [B] int32,
+  out [B, Hq, d] fp32, lse [B, Hq] fp32
 """
 from __future__ import annotations
 
@@ -51,9 +54,22 @@ class WaitsShape(ctypes.Structure):
     ]
 
 
+class WaitsDecodeShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _SP = ctypes.POINTER(WaitsShape)
+_DSP = ctypes.POINTER(WaitsDecodeShape)
 _FP = ctypes.POINTER(ctypes.c_float)
 _IP = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
@@ -68,6 +84,8 @@ _SIGS = {
     "waits_select_workspace_bytes": [_SP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
     "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "waits_decode_workspace_bytes": [_DSP, ctypes.POINTER(ctypes.c_size_t)],
+    "waits_decode": [_DSP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 
@@ -347,3 +365,59 @@ def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None):
     s = score(q, k, cu_seqlens, a, b, scale)
     idx, kc, vc = select_compact(s, k, v, cu_seqlens, budget)
     return s, idx, kc, vc
+
+
+def _decode_shape(q: torch.Tensor, k_cache: torch.Tensor, scale=None) -> WaitsDecodeShape:
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, Hkv, capacity, d]")
+    if k_cache.dtype == torch.bfloat16:
+        dt = WAITS_BF16
+    elif k_cache.dtype == torch.float32:
+        dt = WAITS_F32
+    else:
+        raise TypeError(f"caches must be bfloat16 or float32, got {k_cache.dtype}")
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    if q.shape[0] != k_cache.shape[0] or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q and the caches disagree on batch or head_dim")
+    sh = WaitsDecodeShape()
+    sh.batch, sh.n_q_heads, sh.head_dim = q.shape[0], q.shape[1], q.shape[2]
+    sh.n_kv_heads, sh.capacity = k_cache.shape[1], k_cache.shape[2]
+    sh.dtype = dt
+    sh.scale = 1.0 / math.sqrt(q.shape[2]) if scale is None else float(scale)
+    return sh
+
+
+def decode_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor, scale=None) -> int:
+    """Device workspace bytes decode() needs for these shapes."""
+    sh = _decode_shape(q, k_cache, scale)
+    n = ctypes.c_size_t(0)
+    _check("waits_decode_workspace_bytes", lib().waits_decode_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)))
+    return int(n.value)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, lens: torch.Tensor,
+           scale=None, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """One decoding step's attention over the (compacted) cache: (out, lse).
+
+    q [B, Hq, d]; k_cache / v_cache [B, Hkv, capacity, d] dense (the layout
+    compact() returns); lens int32 [B] on the device (rows attended per
+    sequence).  out fp32 [B, Hq, d]; lse fp32 [B, Hq] (None if not wanted)."""
+    for t in (q, k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("q and the caches must be dense (contiguous)")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must share shape and dtype")
+    if lens.dtype != torch.int32 or lens.shape != (q.shape[0],) or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor of shape [B]")
+    sh = _decode_shape(q, k_cache, scale)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    ws = _workspace(decode_workspace_bytes(q, k_cache, scale), q.device, workspace)
+    _check("waits_decode", lib().waits_decode(
+        ctypes.byref(sh), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(out), _ptr(lse),
+        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
+    return out, lse

@@ -11,7 +11,12 @@ time), the dominant kernel's roofline fraction (per-kernel times from HIP
 events on the stream the library launches on), and the CPU oracle timed on
 a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 8b|1b|long|mistral]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload 8b|1b|long|long_snap|long_tova|mistral|decode]
+
+``--workload decode`` measures the step after the path instead: one decoding
+step's attention over the compacted cache (64 sequences of the Llama-3.1-8B
+shape, 2048 kept rows each), against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -29,7 +34,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import ACTIONS, make_batch, make_prompt  # noqa: E402
+from synth import ACTIONS, make_batch, make_decode, make_prompt  # noqa: E402
 
 METRIC = "prompt tokens/s per layer for WAITS score+select+compact; % bf16 MFMA peak"
 UNIT = "tokens/s/layer"
@@ -120,6 +125,28 @@ def make_inputs(wl, device):
     return q, k, v, cu
 
 
+def _host_info():
+    """(BLAS threads, BLAS description, CPU model) of this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max([x.get("num_threads", 1) for x in info] or [1])
+        blas = ",".join(sorted({f"{x.get('internal_api', '?')}x{x.get('num_threads', '?')}"
+                                for x in info}))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads, blas = 1, "unknown"
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, blas, cpu
+
+
 def cpu_baseline(wl, budget_s: float):
     """The float64 oracle, as it stands, on a bounded sample of the workload:
     whole sequences (all KV heads), taken in order until about ``budget_s``
@@ -143,23 +170,7 @@ def cpu_baseline(wl, budget_s: float):
         used += 1
         if spent >= budget_s:
             break
-    try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        threads = max([x.get("num_threads", 1) for x in info] or [1])
-        blas = ",".join(sorted({f"{x.get('internal_api', '?')}x{x.get('num_threads', '?')}"
-                                for x in info}))
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads, blas = 1, "unknown"
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    threads, blas, cpu = _host_info()
     return {"value": done_tokens / spent, "unit": UNIT, "cores": threads, "kind": "oracle",
             "sample": f"first {used} of {len(wl['lengths'])} sequences of the workload "
                       f"({done_tokens} tokens, all {wl['hkv']} KV heads), float64 numpy oracle "
@@ -285,13 +296,83 @@ def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
     print(json.dumps(rec, indent=1), flush=True)
 
 
+DECODE_WL = dict(desc="decode over the compacted cache: 64 sequences, Llama-3.1-8B shape "
+                      "(32/8/128), 2048 kept rows per KV head, one new token each",
+                 batch=64, hq=32, hkv=8, d=128, cap=2048, seed=4242)
+
+
+def decode_bench(args):
+    """One decoding step's attention for a batch over its compacted cache:
+    value = new tokens per second (one per sequence), roofline against HBM
+    (K and V rows read once, plus q, out and lse)."""
+    import torch
+    import attention_score_eviction_amd as W
+    from oracle import decode_oracle as dec
+
+    wl = DECODE_WL
+    bsz, hq, hkv, d, cap = wl["batch"], wl["hq"], wl["hkv"], wl["d"], wl["cap"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    x = make_decode(wl["seed"], bsz, hq, hkv, cap, d, "bf16")
+    t_gen = time.perf_counter() - t_gen
+    q, k, v = (torch.from_numpy(b).view(torch.bfloat16).to(dev) for b in (x.q_bits, x.k_bits, x.v_bits))
+    lens = torch.full((bsz,), cap, dtype=torch.int32, device=dev)
+    out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(W.waits.decode_workspace_bytes(q, k), 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        W.decode(q, k, v, lens, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        W.decode(q, k, v, lens, out=out, lse=lse, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_kernel = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    nbytes = 2 * bsz * hkv * cap * d * 2 + bsz * hq * d * 2 + bsz * hq * (d + 1) * 4
+    roof = {"bound": "hbm", "kernel": "decode", "achieved": nbytes / (ms_kernel * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    res = {
+        "metric": "decode tokens/s over the compacted cache (one new token per sequence, one layer)",
+        "value": bsz / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["desc"], "sequences": bsz, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "cache_rows": cap, "parallelism": "single GPU"},
+        "roofline": roof, "kernels_us": {"decode": ms_kernel * 1e3},
+        "algorithmic": {"bytes_per_step": nbytes}, "input_gen_s": t_gen, "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        scale = float(np.float32(1 / math.sqrt(d)))
+        done, spent = 0, 0.0
+        lens_h = [cap] * bsz
+        while spent < min(args.cpu_budget_s, 10.0) and done < bsz:
+            t1 = time.perf_counter()
+            dec.waits_decode(x.q[done:done + 1], x.k[done:done + 1], x.v[done:done + 1],
+                             lens_h[done:done + 1], scale)
+            spent += time.perf_counter() - t1
+            done += 1
+        threads, blas, cpu = _host_info()
+        res["cpu_baseline"] = {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"first {done} of {bsz} sequences, float64 numpy decode oracle, "
+                                         f"{spent:.1f} s; BLAS {blas}; {cpu}"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b",
-                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral"])
+                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -311,6 +392,9 @@ def main():
               "build runs on a single MI355X; multi-GPU sharding is design-only.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "decode":
+        decode_bench(args)
+        return
 
     import torch
     import attention_score_eviction_amd as W

@@ -189,6 +189,53 @@ int waits_select_compact(const waits_shape* shape, const float* scores,
                          int32_t* idx, void* k_out, void* v_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Decode attention over the compacted cache
+ * -----------------------------------------
+ * README "Quickstart": after init_cache compresses the prompt's cache,
+ * generation runs on it, so every decoding step attends over the kept rows
+ * (and the rows generation appends after them).  The attention is ordinary
+ * scaled dot-product attention of the step's one query per query head:
+ *   out[i, g, :] = sum_{j < len[i]} softmax_j(scale <q[i, g], K[i, h, j]>) V[i, h, j]
+ *   lse[i, g]    = ln sum_{j < len[i]} exp(scale <q[i, g], K[i, h, j]>),   h = g / G
+ * with no mask inside the cache and no position change (cached keys carry
+ * their own).  An empty cache (len = 0) gives out = 0 and lse = -inf.
+ *
+ * Layouts (all dense, device, 16-byte-aligned base pointers for q and the
+ * caches):
+ *   q        [batch, n_q_heads, head_dim]              (dtype)
+ *   k_cache  [batch, n_kv_heads, capacity, head_dim]   (dtype; the layout
+ *   v_cache   waits_compact writes, with capacity = select_budget, or a
+ *             larger capacity whose rows past the kept ones hold new tokens)
+ *   lens     int32 [batch]: rows attended per sequence; values outside
+ *            [0, capacity] are clamped to it
+ *   out      fp32 [batch, n_q_heads, head_dim]
+ *   lse      fp32 [batch, n_q_heads], or NULL
+ * dtype WAITS_BF16: bf16 q and caches, products accumulated in fp32, the
+ * probabilities and the weighted sum of V in fp32; WAITS_F32: fp32
+ * throughout.  Ownership, stream and error rules are those of the rest of
+ * this header.
+ */
+typedef struct waits_decode_shape {
+  int32_t batch;       /* number of sequences, >= 1                        */
+  int32_t n_q_heads;   /* >= 1, multiple of n_kv_heads                     */
+  int32_t n_kv_heads;  /* >= 1                                             */
+  int32_t head_dim;    /* 64 or 128                                        */
+  int32_t dtype;       /* WAITS_BF16 or WAITS_F32                          */
+  int32_t capacity;    /* cache rows per (sequence, KV head), 1 .. 2^20    */
+  float scale;         /* softmax scale, finite > 0 (1/sqrt(head_dim))     */
+} waits_decode_shape;
+
+/* Bytes of device workspace waits_decode needs (0 when every (sequence,
+ * KV head) runs as one work item; otherwise room for per-split partials). */
+int waits_decode_workspace_bytes(const waits_decode_shape* shape, size_t* bytes);
+
+/* One decoding step's attention for a batch, as defined above.  workspace:
+ * device, 16-byte aligned, >= waits_decode_workspace_bytes (NULL if 0). */
+int waits_decode(const waits_decode_shape* shape, const void* q, const void* k_cache,
+                 const void* v_cache, const int32_t* lens, float* out, float* lse,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a WAITS_E* code. */
 const char* waits_strerror(int code);
 

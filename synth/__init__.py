@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the WAITS prefill KV-selection path.
+"""Seeded synthetic inputs for the WAITS prefill KV-selection path and for
+decode attention over the compacted cache.
 
 This package only draws random tensors and packs them; it holds none of the
 method's arithmetic, so both the CPU oracle's tests and the GPU path's tests
@@ -10,5 +11,7 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     make_prompt,
     make_batch,
+    make_decode,
     Batch,
+    DecodeInputs,
 )

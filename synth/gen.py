@@ -139,3 +139,48 @@ def make_batch(seeds: Sequence[int], lengths: Sequence[int], n_q_heads: int,
     if dtype == "bf16":
         out.q_bits, out.k_bits, out.v_bits = bits
     return out
+
+
+@dataclass
+class DecodeInputs:
+    """One decoding step's inputs: ``q[B, Hq, d]`` and a dense cache
+    ``k/v[B, Hkv, capacity, d]`` (the layout the compaction writes), as
+    float32 values (exact bf16 values for bf16) plus bf16 bit patterns."""
+
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_bits: Optional[np.ndarray] = None
+    k_bits: Optional[np.ndarray] = None
+    v_bits: Optional[np.ndarray] = None
+
+
+def make_decode(seed: int, batch: int, n_q_heads: int, n_kv_heads: int, capacity: int,
+                head_dim: int, dtype: str = "bf16", heavy: bool = True) -> DecodeInputs:
+    """Seeded decode inputs.  Recipe: ``rng = default_rng(seed)``; draw
+    float32 standard normals ``q[B, Hq, d]``, then ``k[B, Hkv, capacity, d]``,
+    then ``v`` of the same shape; with ``heavy``, draw a unit direction ``u``
+    (as for prompts) and the positions ``rng.choice(capacity,
+    max(1, round(0.05 capacity)))`` of every (sequence, KV head), add
+    ``+3 u`` to those keys and to every query; round to bf16 (nearest even)
+    for ``dtype == "bf16"``."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((batch, n_q_heads, head_dim), dtype=np.float32)
+    k = rng.standard_normal((batch, n_kv_heads, capacity, head_dim), dtype=np.float32)
+    v = rng.standard_normal((batch, n_kv_heads, capacity, head_dim), dtype=np.float32)
+    if heavy:
+        u64 = rng.standard_normal(head_dim, dtype=np.float32).astype(np.float64)
+        u = (u64 / np.linalg.norm(u64)).astype(np.float32)
+        cnt = max(1, int(round(0.05 * capacity)))
+        for i in range(batch):
+            for h in range(n_kv_heads):
+                k[i, h, rng.choice(capacity, cnt, replace=False)] += np.float32(3.0) * u
+        q += np.float32(3.0) * u
+    out = DecodeInputs(dtype=dtype, q=q, k=k, v=v)
+    if dtype == "bf16":
+        out.q_bits, out.k_bits, out.v_bits = (bf16_bits(x) for x in (q, k, v))
+        out.q, out.k, out.v = (bf16_bits_to_f32(b) for b in (out.q_bits, out.k_bits, out.v_bits))
+    return out

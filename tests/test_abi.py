@@ -205,3 +205,84 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(W, "LIB_PATH", W.LIB_PATH + ".missing")
     with pytest.raises(RuntimeError, match="missing"):
         W.lib()
+
+
+# ------------------------------------------------------------------ decode ---
+
+def _dshape(batch=2, hq=8, hkv=2, d=128, dtype=W.WAITS_BF16, cap=128, scale=0.088):
+    s = W.WaitsDecodeShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = batch, hq, hkv, d
+    s.dtype, s.capacity, s.scale = dtype, cap, scale
+    return s
+
+
+def _decode(s, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return W.lib().waits_decode(ctypes.byref(s) if s is not None else None, q, k, v, lens, out, lse,
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, W.WAITS_EINVAL),
+    ("n_q_heads", 3, W.WAITS_EINVAL),         # not a multiple of n_kv_heads
+    ("n_kv_heads", 0, W.WAITS_EINVAL),
+    ("head_dim", 96, W.WAITS_EUNSUPPORTED),
+    ("dtype", 5, W.WAITS_EINVAL),
+    ("capacity", 0, W.WAITS_EINVAL),
+    ("capacity", (1 << 20) + 1, W.WAITS_EUNSUPPORTED),
+    ("scale", float("nan"), W.WAITS_EINVAL),
+    ("scale", -1.0, W.WAITS_EINVAL),
+])
+def test_decode_shape_validation(field, value, code):
+    s = _dshape()
+    setattr(s, field, value)
+    assert _decode(s) == code
+    n = ctypes.c_size_t(0)
+    assert W.lib().waits_decode_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == code
+
+
+def test_decode_pointer_and_workspace_validation():
+    s = _dshape()
+    assert _decode(None) == W.WAITS_EINVAL
+    for kw in ("q", "k", "v", "lens", "out"):
+        assert _decode(s, **{kw: None}) == W.WAITS_EINVAL, kw
+    assert _decode(s, q=ctypes.c_void_p(0x100008)) == W.WAITS_EINVAL    # q not 16-byte aligned
+    assert _decode(s, v=ctypes.c_void_p(0x100004)) == W.WAITS_EINVAL    # cache not 16-byte aligned
+    assert _decode(s, out=ctypes.c_void_p(0x100002)) == W.WAITS_EINVAL  # out not 4-byte aligned
+    # a long cache over few sequences is split: the partials need room
+    big = _dshape(batch=1, hkv=1, hq=4, cap=65536)
+    n = ctypes.c_size_t(0)
+    assert W.lib().waits_decode_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == W.WAITS_OK
+    assert n.value > 0
+    assert _decode(big, ws_bytes=n.value - 1) == W.WAITS_EWORKSPACE
+    assert _decode(big, ws=None) == W.WAITS_EWORKSPACE
+    assert _decode(big, ws=ctypes.c_void_p(0x100008)) == W.WAITS_EWORKSPACE  # not 16-byte aligned
+
+
+@pytest.mark.parametrize("batch,hq,hkv,cap,expect_zero", [
+    (32, 32, 8, 128, False),     # 32 layers x 8 heads over a 128-row cache: split in two
+    (256, 32, 8, 128, True),     # many sequences: one item per (sequence, head)
+    (1, 32, 8, 2048, False),
+    (64, 32, 8, 2048, False),
+])
+def test_decode_workspace_sizes(batch, hq, hkv, cap, expect_zero):
+    s = _dshape(batch=batch, hq=hq, hkv=hkv, cap=cap)
+    n = ctypes.c_size_t(0)
+    assert W.lib().waits_decode_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == W.WAITS_OK
+    assert (n.value == 0) == expect_zero
+    if n.value:
+        # at least two splits' (max, sum) and head_dim vector per (sequence, query head)
+        assert n.value >= batch * hq * 2 * (8 + 4 * 128)
+
+
+def test_decode_binding_checks_layouts():
+    q = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    kc = torch.zeros((2, 2, 16, 64), dtype=torch.bfloat16)
+    lens = torch.full((2,), 16, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        W.decode(q, kc.transpose(2, 3), kc, lens)                 # not dense
+    with pytest.raises(ValueError):
+        W.decode(q, kc, kc, lens.to(torch.int64))                 # lens dtype
+    with pytest.raises(TypeError):
+        W.decode(q.float(), kc, kc, lens)                         # mixed dtypes
+    with pytest.raises(ValueError):
+        W.decode(q[:, :, :32].contiguous(), kc, kc, lens)         # head_dim mismatch
