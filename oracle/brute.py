@@ -74,3 +74,20 @@ def decode(qv, kc, vc, scale: float):
     z = math.fsum(ex)
     out = [math.fsum(ex[j] * vc[j][i] for j in range(len(kc))) / z for i in range(d)]
     return out, top + math.log(z)
+
+
+def attention(q, k, v, group: int, scale: float):
+    """Causal attention of one prompt in scalar loops: ``q[n][Hq][d]``,
+    ``k / v[n][Hkv][d]`` nested lists.  Returns ``out[n][Hq][d]`` and
+    ``lse[Hq][n]``.  (Row ``r`` is decode attention over the keys ``<= r``.)"""
+    n, hq = len(q), len(q[0])
+    out = [[None] * hq for _ in range(n)]
+    lse = [[0.0] * n for _ in range(hq)]
+    for g in range(hq):
+        h = g // group
+        for r in range(n):
+            o, z = decode(q[r][g], [k[j][h] for j in range(r + 1)],
+                          [v[j][h] for j in range(r + 1)], scale)
+            out[r][g] = o
+            lse[g][r] = z
+    return out, lse
