@@ -7,6 +7,7 @@ gfx950, C ABI in ``include/waits.h``); ``waits`` is its Python binding.
 from . import waits  # noqa: F401
 from .waits import (  # noqa: F401
     WaitsError,
+    attention,
     colsum,
     compact,
     decode,

@@ -18,6 +18,7 @@
 #include "key_blocks.hpp"
 #include "select_compact.hpp"
 #include "select_wide.hpp"
+#include "attention.hpp"
 
 namespace waits {
 namespace {
@@ -683,6 +684,57 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
   return WAITS_OK;
 }
 
+// Prefill attention forward: one item per (sequence, KV head, block of
+// AT_ROWS packed rows), the blocks with the longest key ranges first.
+int run_attention(const waits_shape* s, const void* q, const void* k, const void* v, void* out,
+                  float* lse, hipStream_t stream) {
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const int hkv = s->n_kv_heads;
+  const int64_t row_bytes = s->kv_stride_tok * elt_bytes(s->dtype);
+  for (int i = 0; i < s->batch; ++i) {
+    const int64_t n = s->cu_seqlens[i + 1] - s->cu_seqlens[i];
+    // buffer loads address a sequence's K/V rows with 32-bit offsets
+    // (the last stage may reach AT_STAGE rows past the sequence end)
+    if ((n + AT_STAGE) * row_bytes > 0x7FFFFFFF || (int64_t)G * n > INT32_MAX / 2) return WAITS_EUNSUPPORTED;
+  }
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    const int hi = std::min(s->batch, lo + MAXB);
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = static_cast<bf16_t*>(out);
+    a.lse = lse;
+    a.st = strides_of(s);
+    a.ntok = s->cu_seqlens[s->batch];
+    a.G = G;
+    a.hkv = hkv;
+    a.hq = s->n_q_heads;
+    a.scale_log2 = s->scale * LOG2E;
+    SeqTable& t = a.tab;
+    t.nb = hi - lo;
+    int items = 0;
+    for (int i = lo; i < hi; ++i) {
+      const int n = (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]);
+      const int j = i - lo;
+      t.n[j] = n;
+      t.tok0[j] = s->cu_seqlens[i];
+      t.nrb[j] = (int)ceil_div((int64_t)G * n, AT_ROWS);
+      t.first[j] = items;
+      items += hkv * t.nrb[j];
+    }
+    t.first[hi - lo] = items;
+    if (items == 0) continue;
+    if (s->head_dim == 64)
+      hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(items), dim3(AT_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(items), dim3(AT_THREADS), 0, stream, a);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
 int run_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
                 int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
   const std::vector<Seq> sq = plan_seqs(s, nullptr, nullptr);
@@ -855,6 +907,18 @@ const char* waits_strerror(int code) {
     case WAITS_EDEVICE: return "HIP runtime refused a kernel launch";
     default: return "unknown WAITS status";
   }
+}
+
+int waits_attention(const waits_shape* s, const void* q, const void* k, const void* v, void* out,
+                    float* lse, hipStream_t stream) {
+  const int rc = check_shape(s, true);
+  if (rc != WAITS_OK) return rc;
+  if (s->dtype != WAITS_BF16) return WAITS_EUNSUPPORTED;
+  if (s->cu_seqlens[s->batch] == 0) return WAITS_OK;
+  if (!q || !k || !v || !out || !is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) ||
+      !is_aligned(out, 16) || (lse && !is_aligned(lse, 4)))
+    return WAITS_EINVAL;
+  return run_attention(s, q, k, v, out, lse, stream);
 }
 
 }  // extern "C"

@@ -84,6 +84,7 @@ _SIGS = {
     "waits_select_workspace_bytes": [_SP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
     "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "waits_attention": [_SP, _P, _P, _P, _P, _P, _P],
     "waits_decode_workspace_bytes": [_DSP, ctypes.POINTER(ctypes.c_size_t)],
     "waits_decode": [_DSP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
@@ -358,6 +359,28 @@ def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_se
         _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
         _stream(k)))
     return idx, k_out, v_out
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, scale=None,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              want_lse: bool = True):
+    """Causal prefill attention with the row log-sum-exp: (out, lse).
+
+    q [T, Hq, d], k / v [T, Hkv, d] bf16 (K and V share strides); out bf16
+    [T, Hq, d] dense; lse fp32 [Hq, T], the same values lse() writes."""
+    _last_dim_contiguous(q, k, v)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    m = _Marshal(cu_seqlens, q, k, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be a dense tensor shaped and typed like q")
+    if lse is None and want_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    _check("waits_attention", lib().waits_attention(
+        m.sp, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse
 
 
 def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None):

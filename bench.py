@@ -12,11 +12,17 @@ events on the stream the library launches on), and the CPU oracle timed on
 a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload 8b|1b|long|long_snap|long_tova|mistral|decode]
+                    [--workload 8b|1b|long|long_snap|long_tova|mistral|decode|fused]
 
 ``--workload decode`` measures the step after the path instead: one decoding
 step's attention over the compacted cache (64 sequences of the Llama-3.1-8B
 shape, 2048 kept rows each), against the HBM roofline.
+
+``--workload fused`` runs the headline batch the way a model's attention call
+would: the prefill attention forward writes out and the row lse, and the
+WAITS scores take that lse (pass 2 only), then select+compact.  The line
+reports the attention kernel against the MFMA roofline, the WAITS marginal
+cost (pass 2 + select/compact) and pass 1's time, which the fusion saves.
 """
 from __future__ import annotations
 
@@ -366,13 +372,98 @@ def decode_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def fused_bench(args):
+    """Headline batch through the attention forward (out + lse), then pass 2
+    and select+compact.  value = layer tokens per second of the whole step."""
+    import torch
+    import attention_score_eviction_amd as W
+
+    wl = workload("8b")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    q, k, v, cu = make_inputs(wl, dev)
+    t_gen = time.perf_counter() - t_gen
+    a, b, budget = wl["a"], wl["b"], wl["budget"]
+    T, hq, hkv, d = int(cu[-1]), wl["hq"], wl["hkv"], wl["d"]
+    B = len(wl["lengths"])
+    out = torch.empty_like(q)
+    lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
+    lse1 = torch.empty_like(lse)
+    ws = torch.empty(max(W.waits.lse_workspace_bytes(q, k, cu, a, b),
+                         W.waits.colsum_workspace_bytes(q, k, cu, a, b), 256), dtype=torch.uint8, device=dev)
+    scores = torch.empty((hkv, T), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, hkv, budget), dtype=torch.int32, device=dev)
+    kc = torch.empty((B, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    sel_ws = torch.empty(max(W.waits.select_workspace_bytes(cu, hkv, budget), 256), dtype=torch.uint8,
+                         device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        W.attention(q, k, v, cu, out=out, lse=lse)
+        if e: e[1].record(stream)
+        W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws)
+        if e: e[2].record(stream)
+        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = ["attention", "pass2_colsum", "select_compact"]
+    per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+           for j, nm in enumerate(names)}
+    # pass 1 on its own, for the saving the fusion brings (not part of the step)
+    p1 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    W.lse(q, k, cu, a, b, out=lse1, workspace=ws)
+    p1[0].record(stream)
+    for _ in range(3):
+        W.lse(q, k, cu, a, b, out=lse1, workspace=ws)
+    p1[1].record(stream)
+    torch.cuda.synchronize()
+    pass1_ms = p1[0].elapsed_time(p1[1]) / 3
+    n = wl["lengths"][0]
+    att_flops = 4.0 * d * hq * (n * (n + 1) / 2) * B          # QK^T and PV over the causal triangle
+    flops_pass, _, sel_bytes, cmp_bytes = algorithmic_work(wl)
+    roof = {"bound": "mfma", "kernel": "attention",
+            "achieved": att_flops / (per["attention"] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    res = {
+        "metric": "prompt tokens/s per layer for attention forward + WAITS pass 2 + select+compact",
+        "value": float(sum(wl["lengths"])) / (ms_step * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["desc"] + ", with the prefill attention forward supplying lse",
+                   "sequences": B, "tokens_per_step": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+                   "select_budget": budget, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels_us": {nm: per[nm] * 1e3 for nm in names},
+        "waits_marginal_us": (per["pass2_colsum"] + per["select_compact"]) * 1e3,
+        "pass1_saved_us": pass1_ms * 1e3,
+        "algorithmic": {"attention_flops": att_flops, "pass2_flops": flops_pass,
+                        "select_compact_bytes": sel_bytes + cmp_bytes},
+        "input_gen_s": t_gen, "host": platform.node(),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b",
-                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode"])
+                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode", "fused"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -394,6 +485,9 @@ def main():
         sys.exit(2)
     if args.workload == "decode":
         decode_bench(args)
+        return
+    if args.workload == "fused":
+        fused_bench(args)
         return
 
     import torch

@@ -140,6 +140,26 @@ int waits_score(const waits_shape* shape, const void* q, const void* k,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Prefill attention forward with the row log-sum-exp.  README "Quickstart":
+ * the method runs inside the model's attention call; introduction: the
+ * score is built from the causal softmax of every prompt row.  The attention
+ * forward computes each row's normaliser anyway, so it writes it out: for
+ * every query row q (t = t0 + q, t0 = cu_seqlens[i]) and query head g,
+ *   out[(t * n_q_heads + g) * head_dim + e]
+ *       = sum_{k <= q} softmax_k(scale <Q[t, g], K[t0 + k, g / G]>) V[t0 + k, g / G, e]
+ *   lse[g * T + t] = ln sum_{k <= q} exp(scale <Q[t, g], K[t0 + k, g / G]>)
+ * lse equals what waits_lse writes at every row, so waits_colsum can take it
+ * directly and the WAITS scores then need no pass 1 of their own.
+ * out: device bf16, dense [T, n_q_heads, head_dim], 16-byte aligned.  lse:
+ * device fp32 [n_q_heads, T], or NULL.  V shares K's strides.  dtype must be
+ * WAITS_BF16 (WAITS_F32: WAITS_EUNSUPPORTED); a sequence's K/V rows must span
+ * less than 2^31 bytes (else WAITS_EUNSUPPORTED).  Softmax sums and out
+ * accumulate in fp32; P is rounded to bf16 for the P V product.
+ */
+int waits_attention(const waits_shape* shape, const void* q, const void* k, const void* v,
+                    void* out, float* lse, hipStream_t stream);
+
+/*
  * Top-k selection (README "Repository layout": top-k selector): for every
  * sequence i and KV head h, the min(N_i, select_budget) keys with the
  * largest score, ties to the lower position, written in ascending position
