@@ -15,8 +15,10 @@
 //      place, and their sum (fp32);
 //   C. o[g] += p[g][j] * V[j] on the VALU in fp32 (p never leaves fp32):
 //      lanes cover a row in 16-byte chunks, so each load instruction reads
-//      whole rows; four rows in flight per lane; then a sum over the lanes
+//      whole rows; DEC_VU rows in flight per lane; then a sum over the lanes
 //      of one chunk and over the waves.
+// Phases A and C keep several tiles / rows of loads in flight per wave so
+// that HBM latency is covered within each work item.
 // One split writes out / lse directly; several write (max, sum, o) partials
 // that decode_combine_kernel merges.  Work is HBM-bound: K and V rows are
 // read once, everything else is small.
@@ -30,6 +32,8 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = DEC_THREADS / WAVE;
 constexpr int DEC_MAX_KS = 1024;     // keys per work item (LDS score table)
 constexpr int DEC_MAX_SPLITS = 1024; // splits per (sequence, query head)
+constexpr int DEC_TU = 4;            // score tiles per wave with loads in flight together
+constexpr int DEC_VU = 8;            // V rows per lane with loads in flight together
 
 struct DecodeArgs {
   const void* q;         // [B, Hq, D]
@@ -100,30 +104,39 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
       const u32x4 x = ld16(qbase + (int64_t)min(c16, gn - 1) * ROWB + (4 * s + g4) * 16);
       qf[s] = c16 < gn ? x : u32x4{0u, 0u, 0u, 0u};
     }
-    for (int t = wave; t * 16 < nk; t += DEC_WAVES) {
-      const int row = min(kbeg + t * 16 + c16, len - 1);  // rows past the item are loaded, not used
-      const unsigned char* kr = kbase + (int64_t)row * ROWB;
-      u32x4 kf[NCH];
+    // DEC_TU tiles per wave and step: their loads are all in flight before
+    // the first MFMA (one tile at a time leaves HBM latency exposed)
+    for (int t0 = wave; t0 * 16 < nk; t0 += DEC_WAVES * DEC_TU) {
+      u32x4 kf[DEC_TU][NCH];
 #pragma unroll
-      for (int s = 0; s < NCH; ++s) kf[s] = ld16(kr + (4 * s + g4) * 16);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < DEC_TU; ++r) {
+        const int row = min(kbeg + (t0 + r * DEC_WAVES) * 16 + c16, len - 1);  // past the item: loaded, unused
+        const unsigned char* kr = kbase + (int64_t)row * ROWB;
 #pragma unroll
-      for (int s = 0; s < NCH; ++s) {
-        if constexpr (BF) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[s]),
-                                                        __builtin_bit_cast(bf16x8, qf[s]), acc, 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[s][u]), __uint_as_float(qf[s][u]),
-                                                       acc, 0, 0, 0);
-        }
+        for (int s = 0; s < NCH; ++s) kf[r][s] = ld16(kr + (4 * s + g4) * 16);
       }
-      if (c16 < GC) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = t * 16 + 4 * g4 + i;
-          if (j < nk) sc[j][c16] = acc[i] * a.scale_log2;
+      for (int r = 0; r < DEC_TU; ++r) {
+        const int t = t0 + r * DEC_WAVES;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NCH; ++s) {
+          if constexpr (BF) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[r][s]),
+                                                          __builtin_bit_cast(bf16x8, qf[s]), acc, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[r][s][u]), __uint_as_float(qf[s][u]),
+                                                         acc, 0, 0, 0);
+          }
+        }
+        if (c16 < GC) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = t * 16 + 4 * g4 + i;
+            if (j < nk) sc[j][c16] = acc[i] * a.scale_log2;
+          }
         }
       }
     }
@@ -157,15 +170,15 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
 #pragma unroll
     for (int e = 0; e < EPC; ++e) o[g][e] = 0.f;
   constexpr int STEP = DEC_WAVES * KPW;
-  for (int j0 = wave * KPW + slot; j0 < nk; j0 += 4 * STEP) {
-    u32x4 vv[4];
+  for (int j0 = wave * KPW + slot; j0 < nk; j0 += DEC_VU * STEP) {
+    u32x4 vv[DEC_VU];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < DEC_VU; ++r) {
       const int j = min(j0 + r * STEP, nk - 1);  // past the item: a valid row, weight 0
       vv[r] = ld16(vbase + (int64_t)(kbeg + j) * ROWB + ch * 16);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < DEC_VU; ++r) {
       const int j = j0 + r * STEP;
       float p[GC];
 #pragma unroll

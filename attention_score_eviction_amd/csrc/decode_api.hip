@@ -15,7 +15,7 @@ namespace waits {
 namespace {
 
 constexpr int DEC_NUM_CU = 256;
-constexpr int DEC_MIN_KS = 64;                       // shortest key split
+constexpr int DEC_MIN_KS = 256;                      // shortest key split (shorter caches: one)
 constexpr int DEC_MAX_CAP = DEC_MAX_KS * DEC_MAX_SPLITS;
 
 struct DecPlan {
@@ -39,7 +39,9 @@ int check_decode_shape(const waits_decode_shape* s) {
 
 // Query heads per item: the group (rounded up to a power of two) while it
 // fits 8, so every K/V row is read once per split; larger groups in chunks
-// of 8.  Key splits: about 4 items per CU over the batch, 64..1024 keys each.
+// of 8.  Key splits: about 4 items per CU over the batch, 256..1024 keys each
+// (a shorter cache is one split: its combine launch would cost more than the
+// parallelism it buys).
 DecPlan plan_decode(const waits_decode_shape* s) {
   DecPlan p;
   const int G = s->n_q_heads / s->n_kv_heads;
@@ -49,7 +51,8 @@ DecPlan plan_decode(const waits_decode_shape* s) {
   int64_t ks = cdiv(rows, 4 * DEC_NUM_CU);
   ks = cdiv(ks, 16) * 16;
   ks = std::max<int64_t>(ks, cdiv(s->capacity, DEC_MAX_SPLITS));
-  p.ks = (int)std::min<int64_t>(std::max<int64_t>(ks, DEC_MIN_KS), DEC_MAX_KS);
+  const int64_t min_ks = std::min<int64_t>(DEC_MIN_KS, cdiv(s->capacity, 16) * 16);
+  p.ks = (int)std::min<int64_t>(std::max<int64_t>(ks, min_ks), DEC_MAX_KS);
   p.nsplit = (int)cdiv(s->capacity, p.ks);
   if (p.nsplit > 1) {
     const size_t slots = (size_t)s->batch * s->n_q_heads * p.nsplit;

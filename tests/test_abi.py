@@ -259,8 +259,9 @@ def test_decode_pointer_and_workspace_validation():
 
 
 @pytest.mark.parametrize("batch,hq,hkv,cap,expect_zero", [
-    (32, 32, 8, 128, False),     # 32 layers x 8 heads over a 128-row cache: split in two
+    (32, 32, 8, 128, True),      # a 128-row cache is one split (no combine)
     (256, 32, 8, 128, True),     # many sequences: one item per (sequence, head)
+    (4, 32, 8, 1024, False),     # few sequences, longer caches: split for parallelism
     (1, 32, 8, 2048, False),
     (64, 32, 8, 2048, False),
 ])
