@@ -10,8 +10,9 @@
 // Work item = (sequence, KV head, block of AT_ROWS packed rows); packed row r
 // of KV head h is query position r / G of query head h G + r % G, so the G
 // query heads that share K/V rows share the workgroup.  Four waves (one per
-// SIMD, so a wave may hold 512 registers: the O accumulators sit in AGPRs),
-// each with two 32-row tiles that share every K and V fragment it reads.
+// SIMD, so a wave may hold 512 registers: the O accumulators and the Q
+// fragments sit in AGPRs), each with two 32-row tiles that share every K and
+// V fragment it reads.
 // Keys 0 .. the block's last query stream through LDS in 64-key stages: K
 // row-major (padded rows), V transposed (V^T[d][key]) so that it can be the
 // A operand of O^T += V^T P^T; a one-stage register ring keeps the next
@@ -123,6 +124,9 @@ __global__ void __launch_bounds__(AT_THREADS) attn_fwd_kernel(const AttnArgs a) 
     for (int v = 0; v < Geo::NV; ++v) {
       const u32x4 x = ld16(src + 16 * v);
       qf[t][v] = row_ok[t] ? x : u32x4{0u, 0u, 0u, 0u};
+      // Q lives in AGPRs for the whole item: the S^T MFMAs read their B
+      // operand from there directly, leaving the VGPRs to K, P and the ring
+      asm volatile("" : "+a"(qf[t][v]));
     }
   }
 
@@ -191,8 +195,8 @@ __global__ void __launch_bounds__(AT_THREADS) attn_fwd_kernel(const AttnArgs a) 
   for (int t = 0; t < AT_TW; ++t) {
 #pragma unroll
     for (int d = 0; d < NDT; ++d) acc_o[t][d] = f32x16{};
-    // padding rows (every key masked) keep a finite reference, so their
-    // exponentials are exact zeros on the fast path
+    // padding rows (never written) keep a finite reference, so that they
+    // never send a sub-tile down the rare path
     mref[t] = row_ok[t] ? -INFINITY : 0.f;
     lsum[t] = 0.f;
 #pragma unroll
@@ -201,10 +205,11 @@ __global__ void __launch_bounds__(AT_THREADS) attn_fwd_kernel(const AttnArgs a) 
   u32x4 kf[Geo::NV];
 
   // Softmax of sub-tile j (acc_s) into the bf16 P^T operands pb.  diag
-  // (wave-uniform): the sub-tile may reach past a row's position, so keys
-  // after it are zeroed after the exponentials (one short branch instead of a
-  // second copy of the whole sub-tile); a tile whose rows all precede the
-  // sub-tile gets P = 0.
+  // (wave-uniform): the sub-tile may reach past a row's position.  The fast
+  // path has no masks: a diagonal sub-tile (about one in a hundred) goes
+  // through the rare path, which recomputes its exponentials with keys after
+  // each row's position masked; a tile whose rows all precede the sub-tile
+  // gets P = 0 there.
   auto epilogue = [&](int j, bool diag) __attribute__((always_inline)) {
     const int ktj = j * TILE;
     // masked logit (log2 units) for the rare path
@@ -212,32 +217,26 @@ __global__ void __launch_bounds__(AT_THREADS) attn_fwd_kernel(const AttnArgs a) 
       const float s = acc_s[t][v] * cl2;
       return (diag && ktj + out_row(v, hf) > qpos[t]) ? -INFINITY : s;
     };
-    float pv[AT_TW][16];
+    float pv[AT_TW][16], lold[AT_TW];
 #pragma unroll
     for (int t = 0; t < AT_TW; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) pv[t][v] = fast_exp2(fmaf(acc_s[t][v], cl2, -mref[t]));
-    if (diag) {
-#pragma unroll
-      for (int t = 0; t < AT_TW; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (ktj + out_row(v, hf) > qpos[t]) pv[t][v] = 0.f;
-    }
-    bool ok = true;
+    bool ok = !diag;
 #pragma unroll
     for (int t = 0; t < AT_TW; ++t) {
+      lold[t] = lsum[t];
       const float ln = lsum[t] + sum16(pv[t]);
       ok = ok && ln < 0x1p64f;
       lsum[t] = ln;
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) != 0, 0)) {
-      // Rare (a row's first keys, or a much larger score later): move the
-      // reference of both lanes of every row to their common max and rescale
-      // what was summed against the old one.
+      // Rare (a diagonal sub-tile, a row's first keys, or a much larger
+      // score later): move the reference of both lanes of every row to their
+      // common max and rescale what was summed against the old one.
 #pragma unroll
       for (int t = 0; t < AT_TW; ++t) {
-        lsum[t] -= sum16(pv[t]);
+        lsum[t] = lold[t];
         float mx = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, logit(t, v));
@@ -248,15 +247,15 @@ __global__ void __launch_bounds__(AT_THREADS) attn_fwd_kernel(const AttnArgs a) 
 #pragma unroll
           for (int v = 0; v < 16; ++v) pv[t][v] = 0.f;
         } else {
-          if (mref[t] != -INFINITY) {
+          if (mref[t] == -INFINITY) {
+            lsum[t] = 0.f;
+          } else if (mnew != mref[t]) {
             const float alpha = fast_exp2(mref[t] - mnew);
 #pragma unroll
             for (int d = 0; d < NDT; ++d)
 #pragma unroll
               for (int v = 0; v < 16; ++v) acc_o[t][d][v] *= alpha;
             lsum[t] *= alpha;
-          } else {
-            lsum[t] = 0.f;
           }
 #pragma unroll
           for (int v = 0; v < 16; ++v) pv[t][v] = fast_exp2(logit(t, v) - mnew);
