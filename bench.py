@@ -11,7 +11,13 @@ time), the dominant kernel's roofline fraction (per-kernel times from HIP
 events on the stream the library launches on), and the CPU oracle timed on
 a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W]
+Each stage of a step (pass 1, pass 2, select+compact) is one library call
+per step; ``--graph`` instead captures each stage once into a HIP graph and
+replays it (the library is capture-safe: no allocation, memset or host sync
+inside its calls).  On ROCm 7.2 a replay costs about 1 us more per kernel node
+than direct launches, so the default is direct calls.
+
+    python bench.py [--steps K] [--warmup W] [--graph]
                     [--workload 8b|1b|long|long_snap|long_tova|mistral|decode|fused]
 
 ``--workload decode`` measures the step after the path instead: one decoding
@@ -27,6 +33,8 @@ cost (pass 2 + select/compact) and pass 1's time, which the fusion saves.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import math
 import os
@@ -302,6 +310,48 @@ def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
     print(json.dumps(rec, indent=1), flush=True)
 
 
+def stage_runners(fns, graph: bool):
+    """One callable per stage of a step: the library calls themselves, or,
+    with ``graph``, the replay of a HIP graph (torch.cuda.CUDAGraph) captured
+    once from them; every replay launches all of the stage's kernels on the
+    current stream, with the host-side planning done once at capture."""
+    if not graph:
+        return list(fns)
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return [g.replay for g in graphs]
+
+
+@contextlib.contextmanager
+def no_gc():
+    """Python's cyclic collector off for the timed region (collected once
+    before it): a full collection of torch's object graph takes 30-40 ms on
+    the host, and the GPU drains its queue and idles while one runs."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
+def launch_mode(args) -> str:
+    return "one HIP graph replay per stage" if args.graph else "direct library calls"
+
+
 DECODE_WL = dict(desc="decode over the compacted cache: 64 sequences, Llama-3.1-8B shape "
                       "(32/8/128), 2048 kept rows per KV head, one new token each",
                  batch=64, hq=32, hkv=8, d=128, cap=2048, seed=4242)
@@ -329,16 +379,18 @@ def decode_bench(args):
     ws = torch.empty(max(W.waits.decode_workspace_bytes(q, k), 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for _ in range(args.warmup):
-        W.decode(q, k, v, lens, out=out, lse=lse, workspace=ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        W.decode(q, k, v, lens, out=out, lse=lse, workspace=ws)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    (run,) = stage_runners([lambda: W.decode(q, k, v, lens, out=out, lse=lse, workspace=ws)], args.graph)
+    with no_gc():
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            run()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_kernel = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     nbytes = 2 * bsz * hkv * cap * d * 2 + bsz * hq * d * 2 + bsz * hq * (d + 1) * 4
     roof = {"bound": "hbm", "kernel": "decode", "achieved": nbytes / (ms_kernel * 1e-3) / 1e9,
@@ -351,7 +403,8 @@ def decode_bench(args):
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["desc"], "sequences": bsz, "q_heads": hq, "kv_heads": hkv,
-                   "head_dim": d, "cache_rows": cap, "parallelism": "single GPU"},
+                   "head_dim": d, "cache_rows": cap, "parallelism": "single GPU",
+                   "launch": launch_mode(args)},
         "roofline": roof, "kernels_us": {"decode": ms_kernel * 1e3},
         "algorithmic": {"bytes_per_step": nbytes}, "input_gen_s": t_gen, "host": platform.node(),
     }
@@ -401,34 +454,39 @@ def fused_bench(args):
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
-    def step(e=None):
-        if e: e[0].record(stream)
-        W.attention(q, k, v, cu, out=out, lse=lse)
-        if e: e[1].record(stream)
-        W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws)
-        if e: e[2].record(stream)
-        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws)
-        if e: e[3].record(stream)
+    runs = stage_runners([
+        lambda: W.attention(q, k, v, cu, out=out, lse=lse),
+        lambda: W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws),
+        lambda: W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws),
+    ], args.graph)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
+    def step(e=None):
+        for j, run in enumerate(runs):
+            if e: e[j].record(stream)
+            run()
+        if e: e[len(runs)].record(stream)
+
+    with no_gc():
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     names = ["attention", "pass2_colsum", "select_compact"]
     per = {nm: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            for j, nm in enumerate(names)}
     # pass 1 on its own, for the saving the fusion brings (not part of the step)
     p1 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    W.lse(q, k, cu, a, b, out=lse1, workspace=ws)
-    p1[0].record(stream)
-    for _ in range(3):
+    with no_gc():
         W.lse(q, k, cu, a, b, out=lse1, workspace=ws)
-    p1[1].record(stream)
-    torch.cuda.synchronize()
+        p1[0].record(stream)
+        for _ in range(3):
+            W.lse(q, k, cu, a, b, out=lse1, workspace=ws)
+        p1[1].record(stream)
+        torch.cuda.synchronize()
     pass1_ms = p1[0].elapsed_time(p1[1]) / 3
     n = wl["lengths"][0]
     att_flops = 4.0 * d * hq * (n * (n + 1) / 2) * B          # QK^T and PV over the causal triangle
@@ -445,7 +503,7 @@ def fused_bench(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["desc"] + ", with the prefill attention forward supplying lse",
                    "sequences": B, "tokens_per_step": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
-                   "select_budget": budget, "parallelism": "single GPU"},
+                   "select_budget": budget, "parallelism": "single GPU", "launch": launch_mode(args)},
         "roofline": roof,
         "kernels_us": {nm: per[nm] * 1e3 for nm in names},
         "waits_marginal_us": (per["pass2_colsum"] + per["select_compact"]) * 1e3,
@@ -466,6 +524,8 @@ def main():
                     choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode", "fused"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each stage from a captured HIP graph instead of calling the library")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     ap.add_argument("--counters-from", metavar="DIR",
@@ -517,22 +577,26 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
-    def step(e=None):
-        if e: e[0].record(stream)
-        W.lse(q, k, cu, a, b, out=lse, workspace=ws)
-        if e: e[1].record(stream)
-        W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws)
-        if e: e[2].record(stream)
-        W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws)
-        if e: e[3].record(stream)
+    runs = stage_runners([
+        lambda: W.lse(q, k, cu, a, b, out=lse, workspace=ws),
+        lambda: W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws),
+        lambda: W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws),
+    ], args.graph)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
+    def step(e=None):
+        for j, run in enumerate(runs):
+            if e: e[j].record(stream)
+            run()
+        if e: e[len(runs)].record(stream)
+
+    with no_gc():
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
@@ -580,7 +644,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["desc"], "sequences": B, "tokens_per_step": T,
                    "q_heads": hq, "kv_heads": hkv, "head_dim": d, "select_budget": budget,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "launch": launch_mode(args)},
         "roofline": roof,
         "passes_mfma_frac": 2 * flops_pass / (passes_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "select_compact_hbm_frac": (sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
