@@ -518,8 +518,10 @@ def fused_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the clock ramps up over the first ~20 ms of sustained load (about 20
+    # headline steps, 1.26 -> 1.01 ms), so the timed steps start after that
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="8b",
                     choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode", "fused"])
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
