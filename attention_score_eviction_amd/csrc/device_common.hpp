@@ -182,6 +182,20 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, WAVE);
 }
 
+// x plus its value in lane l ^ 16 (add_xor16) or l ^ 32 (add_xor32), in
+// every lane, without LDS: v_permlane16_swap / v_permlane32_swap exchange
+// 16-lane (32-lane) halves between two registers; both hold x, so each lane
+// ends with its own value and its partner's, whose sum (commutative) equals
+// x + __shfl_xor(x, 16 / 32) bit for bit.
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Which sequence a flat work-item index belongs to: first[i] is the first item
 // of sequence i, first[nb] the total.  nb <= MAXB, so a scan is cheap.
 __device__ __forceinline__ int find_seq(const int32_t* first, int nb, int item) {

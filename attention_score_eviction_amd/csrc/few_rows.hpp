@@ -364,7 +364,7 @@ few_rows_kernel(const FrArgs args) {
   };
   // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)
   auto red_store = [&](int j, float csum) {
-    csum += wave_xor32(csum);
+    csum = add_xor32(csum);
     if (hf == 0) red[j & (2 * FR_SUB - 1)][wave][col] = csum;
   };
   auto flush = [&](int j) {

@@ -341,9 +341,7 @@ few_rows16_kernel(const FrArgs args) {
   auto red_store = [&](int j, const float* csum) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      float sv = csum[kt];
-      sv += __shfl_xor(sv, 16, WAVE);
-      sv += __shfl_xor(sv, 32, WAVE);
+      const float sv = add_xor32(add_xor16(csum[kt]));
       if (g4 == 0) red[j & (2 * FR_SUB - 1)][wave][kt * T16 + c16] = sv;
     }
   };
