@@ -98,9 +98,15 @@ def long_prompt():
     return make_prompt(2, 131072, 32, 8, 128, heavy=True, dtype="bf16")
 
 
-@pytest.mark.parametrize("a,b", [(math.inf, 16), (1.0, 16), (math.inf, 1)])
+@pytest.mark.parametrize("a,b", [(math.inf, 16), (1.0, 16), (math.inf, 1), (1.0, 1), (1.0, 128),
+                                 (math.inf, 128)])
 def test_long_context_full_size(long_prompt, a, b):
-    # one layer, N=131072, 32/8/128, budget 2048 (few-row regimes: full oracle)
+    # one layer, N=131072, 32/8/128, budget 2048: the a in {1, inf} x b in
+    # {1, 16, 128} sweep of this shape (a = 0 below).  The processed rows are
+    # few (b at a = inf, about b + 70 at a = 1), so the oracle runs in full;
+    # the sweep spans the 16-row kernel (1:1), the 512-row few-rows shape
+    # (inf:128), the smallest shapes (inf:1, inf:16) and row blocks with key
+    # blocks (1:128).
     _say(f"long N=131072 a={a} b={b}")
     _full_check(long_prompt, [a], [b], 2048, weight_floor=1e-30)
 
