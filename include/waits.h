@@ -35,7 +35,8 @@
  *   enqueued; a failed check returns a nonzero WAITS_E* code and enqueues
  *   nothing.  WAITS_EDEVICE reports a launch the HIP runtime refused; faults
  *   inside kernels surface at the caller's next synchronisation.
- * - Per-sequence limits: 0 <= N < 2^23 (so N - b - 0.5 is exact in fp32).
+ * - Per-sequence limits: 0 <= N < 2^22 and 1 <= b <= 2^22 (so N - b - 0.5
+ *   and q - (N - b - 0.5) are exact in fp32); larger values are rejected.
  */
 #ifndef WAITS_H
 #define WAITS_H
@@ -73,8 +74,8 @@ typedef struct waits_shape {
 
 /*
  * a[i], b[i] (HOST arrays [batch]): the forgetting curve of sequence i.
- * a in [0, +inf] (NaN and negative values are rejected); b >= 1 (b > N is
- * allowed and weights every row).  a = +inf is evaluated with IEEE
+ * a in [0, +inf] (NaN and negative values are rejected); 1 <= b <= 2^22
+ * (b > N is allowed and weights every row).  a = +inf is evaluated with IEEE
  * arithmetic: N - b - 0.5 is a half-integer, so w is exactly 0 or 1.
  *
  * Only query rows whose fp32 weight is nonzero can change a score; the
