@@ -50,8 +50,8 @@ struct CombineArgs {
   int64_t T;
   int32_t G;
   int32_t hkv;
-  int32_t team;               // lanes per row (power of two dividing 64)
-  SeqTable tab;               // first[] counts (KV head, packed row) pairs
+  int32_t team[MAXB];         // lanes per row of each sequence (power of two dividing 64)
+  SeqTable tab;               // first[]: first thread of each sequence (multiples of 64)
 };
 
 struct ColsumArgs {

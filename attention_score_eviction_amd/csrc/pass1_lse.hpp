@@ -184,23 +184,27 @@ lse_kernel(const LseArgs args) {
 }
 
 // Merge the per-chunk (max * scale*log2 e, sum) pairs of each row into lse.
-// One thread per (KV head, packed row); a row reads the chunks that start at
-// or before its own position (later chunks hold no key of its causal range).
+// A team of lanes per (KV head, packed row); a row reads the chunks that
+// start at or before its own position (later chunks hold no key of its
+// causal range).
 __global__ void __launch_bounds__(256)
 lse_combine_kernel(const CombineArgs args) {
-  // A team of args.team lanes (a power of two dividing 64) merges one row's
-  // partials: each lane takes every team-th chunk, then the team reduces.
+  // Sequence p's rows take args.team[p] lanes each (a power of two dividing
+  // 64, sized to its chunk count): each lane takes every team-th chunk, then
+  // the team reduces.  Every sequence's threads start on a wave boundary, so
+  // the team size is uniform within a wave.
   const SeqTable& tab = args.tab;
-  const int team = args.team;
   const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int item = gid / team;
-  const int tl = gid - item * team;
-  const bool live = item < tab.first[tab.nb];
-  const int p = find_seq(tab.first, tab.nb, live ? item : 0);
-  const int local = item - tab.first[p];
+  const bool in_range = gid < tab.first[tab.nb];
+  const int p = find_seq(tab.first, tab.nb, in_range ? gid : 0);
+  const int team = args.team[p];
+  const int loc = gid - tab.first[p];
+  const int local = loc / team;  // (KV head, packed row) of the sequence
+  const int tl = loc - local * team;
   const int G = args.G;
   const int N = tab.n[p], q0 = tab.q0[p];
   const int PR = G * (N - q0);
+  const bool live = in_range && local < args.hkv * PR;  // the wave padding holds no row
   const int h = live ? local / PR : 0;
   const int r = live ? local - h * PR : 0;
   const int j = r / G;

@@ -417,20 +417,29 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     cargs.G = G;
     cargs.hkv = hkv;
     cargs.tab = tab;
-    int rows = 0, max_nc = 1;
+    // a team of lanes per row, sized to the sequence's chunk count; every
+    // sequence's threads start on a wave boundary (one lane per row if the
+    // teams would not fit the 32-bit thread index)
+    auto plan_combine = [&](bool teams) {
+      int64_t threads = 0;
+      for (int i = lo; i < hi; ++i) {
+        int team = 1;
+        while (teams && team < 64 && team < v[i].nc / 2) team *= 2;
+        cargs.team[i - lo] = team;
+        cargs.tab.first[i - lo] = (int32_t)std::min<int64_t>(threads, INT32_MAX);
+        if (v[i].nc > 1) threads += ((int64_t)hkv * v[i].pr * team + WAVE - 1) / WAVE * WAVE;
+      }
+      cargs.tab.first[hi - lo] = (int32_t)std::min<int64_t>(threads, INT32_MAX);
+      return threads;
+    };
+    int64_t threads = plan_combine(true);
+    if (threads > INT32_MAX) threads = plan_combine(false);
     for (int i = lo; i < hi; ++i) {
-      cargs.tab.first[i - lo] = rows;
-      if (v[i].nc > 1) rows += hkv * v[i].pr;
-      max_nc = std::max(max_nc, v[i].nc);
       // the few-rows kernel writes every (row, chunk) partial; the lse kernel
       // only the chunks a row reaches
       if (v[i].mode != Mode::WIDE) cargs.tab.kc[i - lo] = 0;
     }
-    cargs.tab.first[hi - lo] = rows;
-    if (rows > 0) {
-      cargs.team = 1;
-      while (cargs.team < 64 && cargs.team < max_nc / 2) cargs.team *= 2;
-      const int64_t threads = (int64_t)rows * cargs.team;
+    if (threads > 0) {
       hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                          stream, cargs);
       if (launched() != WAITS_OK) return WAITS_EDEVICE;
