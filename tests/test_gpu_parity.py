@@ -129,6 +129,21 @@ def test_long_context_h2o_sampled(long_prompt):
     check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, bt.cu_seqlens)
 
 
+@pytest.fixture(scope="module")
+def longest_prompt():
+    return make_prompt(9, (1 << 22) - 1, 1, 1, 64, heavy=True, dtype="bf16")
+
+
+@pytest.mark.parametrize("a,b", [(math.inf, 16), (1.0, 16)])
+def test_longest_accepted_sequence(longest_prompt, a, b):
+    # N = 2^22 - 1, the longest sequence the boundary accepts (one head,
+    # head_dim 64): key ranges cut over many workgroups and merged, chunk
+    # buffer spans near their 2^31-byte bound, and the select over 4M keys in
+    # 4096-key chunks; the processed rows are few, so the oracle runs in full
+    _say(f"longest N=2^22-1 a={a} b={b}")
+    _full_check(longest_prompt, [a], [b], 2048, weight_floor=1e-30)
+
+
 def _mistral_batch(lo, hi, seed=3):
     rng = np.random.default_rng(seed)
     lengths = rng.integers(lo, hi, endpoint=True, size=8)
