@@ -91,10 +91,12 @@ def test_decode_small_shapes(hq, hkv, d, dtype):
 
 
 @pytest.mark.parametrize("cap,lens", [(64, [64]), (65, [65]), (1000, [999]), (4097, [4097]),
-                                      (65536, [65536]), (65536, [40001]), (2048, [1])])
+                                      (65536, [65536]), (65536, [40001]), (2048, [1]),
+                                      (1 << 20, [1 << 20]), (1 << 20, [777777])])
 def test_decode_split_and_combine(cap, lens):
     # one sequence, one KV head: the cache is cut into up to 1024 splits that
-    # the combine kernel merges
+    # the combine kernel merges (2^20 rows: the largest capacity accepted,
+    # every split at its longest)
     _say(f"decode splits cap={cap} lens={lens}")
     x = make_decode(cap % 977, 1, 4, 1, cap, 128, "bf16")
     out, lse = _run(x, lens)
