@@ -124,6 +124,27 @@ def test_attention_llama31_8b_sampled_rows():
     _check_rows(out, lse, ref_out, ref_lse, _vmax(bt, 4), rows=rows)
 
 
+def test_attention_long_context_sampled_rows():
+    # one layer of the long-context shape, N = 131072 (2048 row blocks per KV
+    # head, key ranges up to the whole prompt): sampled rows through the
+    # decode oracle, including both ends and row-block boundaries
+    _say("attention long N=131072 sampled")
+    n = 131072
+    bt = make_prompt(2, n, 32, 8, 128, heavy=True)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    out, lse = _run(bt, scale)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.array([0, 1, 63, 64, 65, 16383, 16384, 65535, 65536, n - 2, n - 1]),
+                                     rng.integers(0, n, size=13)]))
+    ref_out = np.zeros((n, 32, 128))
+    ref_lse = np.zeros((32, n))
+    for r in rows:
+        for g in range(32):
+            o, l = dec.decode_head(bt.q[r, g], bt.k[:r + 1, g // 4], bt.v[:r + 1, g // 4], scale)
+            ref_out[r, g], ref_lse[g, r] = o, l
+    _check_rows(out, lse, ref_out, ref_lse, _vmax(bt, 4), rows=rows)
+
+
 def test_attention_lse_feeds_waits_pass2():
     # The fused flow: lse from the attention call replaces pass 1; the scores,
     # selection and compaction then meet the WAITS bar against the oracle.
