@@ -194,6 +194,18 @@ def test_ragged_small_sizes(n, hq, hkv, d):
         _full_check(bt, [a], [b], 64)
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(3, 1, 64), (6, 2, 128), (10, 2, 64), (14, 2, 128)])
+def test_group_sizes_not_powers_of_two(hq, hkv, d):
+    # G = 3, 3, 5, 7: packed rows interleave the G query heads of a position,
+    # so row tiles, row blocks and key-block row stages start mid-position;
+    # a = 1 runs the few-rows shapes, a = 0 row blocks and key blocks, a = inf
+    # with b = 40 the few-rows shapes at 120..280 packed rows
+    _say(f"group sizes hq={hq} hkv={hkv} d={d}")
+    bt = make_batch([81 + hq, 82 + hq], [3000, 1500], hq, hkv, d, heavy=True)
+    for a, b in [(1.0, 16), (0.0, 1), (math.inf, 40)]:
+        _full_check(bt, [a, a], [b, b], 128)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("a,b", [(math.inf, 65), (math.inf, 96), (math.inf, 97), (1.0, 16),
                                  (math.inf, 112), (math.inf, 113), (math.inf, 128)])
