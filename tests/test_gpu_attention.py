@@ -95,6 +95,16 @@ def test_attention_small_ragged_batch(hq, hkv, d):
     _check_rows(out, lse, ref_out, ref_lse, _vmax(bt, hq // hkv))
 
 
+def test_attention_scale_other_than_default():
+    # a sharp softmax (scale 0.3, logits in the tens) over ragged prompts
+    _say("attention scale 0.3")
+    bt = make_batch([51, 52], [1500, 333], 8, 2, 128, heavy=True)
+    scale = 0.3
+    out, lse = _run(bt, scale)
+    ref_out, ref_lse = att.prefill_attention(bt.q, bt.k, bt.v, bt.cu_seqlens, 8, 2, float(np.float32(scale)))
+    _check_rows(out, lse, ref_out, ref_lse, _vmax(bt, 4))
+
+
 def test_attention_llama32_1b_full():
     # 32/8/64 at N = 2048, every row against the oracle
     _say("attention 1b shape N=2048")

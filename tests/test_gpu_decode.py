@@ -103,6 +103,15 @@ def test_decode_split_and_combine(cap, lens):
     _check(out, lse, x.q, x.k, x.v, lens, float(np.float32(1 / math.sqrt(128))))
 
 
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_decode_scale_other_than_default(scale):
+    _say(f"decode scale {scale}")
+    x = make_decode(31, 4, 32, 8, 3000, 128, "bf16")
+    lens = [3000, 1234, 1, 2999]
+    out, lse = _run(x, lens, scale)
+    _check(out, lse, x.q, x.k, x.v, lens, float(np.float32(scale)))
+
+
 def test_decode_lengths_are_clamped():
     _say("decode clamped lengths")
     x = make_decode(5, 3, 8, 2, 40, 64, "bf16")

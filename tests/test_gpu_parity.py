@@ -194,6 +194,17 @@ def test_ragged_small_sizes(n, hq, hkv, d):
         _full_check(bt, [a], [b], 64)
 
 
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_scale_other_than_default(scale, dtype):
+    # the scale is an argument, not 1/sqrt(d) baked in: a flat (0.05) and a
+    # sharp (0.3, logits in the tens) softmax, every regime of a small batch
+    _say(f"scale {scale} {dtype}")
+    bt = make_batch([91, 92], [2000, 700], 8, 2, 128, heavy=True, dtype=dtype)
+    for a, b in [(1.0, 16), (0.0, 1), (math.inf, 40)]:
+        _full_check(bt, [a, a], [b, b], 128, scale=scale)
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(3, 1, 64), (6, 2, 128), (10, 2, 64), (14, 2, 128)])
 def test_group_sizes_not_powers_of_two(hq, hkv, d):
     # G = 3, 3, 5, 7: packed rows interleave the G query heads of a position,
