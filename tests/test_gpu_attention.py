@@ -198,6 +198,18 @@ def test_attention_head_major_strides_and_determinism():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def test_attention_packed_qkv_views():
+    # Q, K and V as views into one [T, Hq + 2 Hkv, d] buffer
+    _say("attention packed qkv views")
+    bt = make_batch([25, 26], [900, 400], 8, 2, 128, heavy=True)
+    q, k, v = to_device(bt)
+    qkv = torch.cat([q, k, v], dim=1).contiguous()
+    o1, l1 = W.attention(q, k, v, bt.cu_seqlens)
+    o2, l2 = W.attention(qkv[:, :8], qkv[:, 8:10], qkv[:, 10:12], bt.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_attention_rejects_fp32():
     bt = make_prompt(2, 64, 2, 1, 64, heavy=False, dtype="f32")
     q, k, v = to_device(bt)

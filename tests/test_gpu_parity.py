@@ -294,6 +294,23 @@ def test_head_major_strides_match_token_major(a, b):
     assert torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1), (math.inf, 40)])
+def test_packed_qkv_views_match_separate_tensors(a, b):
+    # a model's fused projection: one [T, Hq + 2 Hkv, d] buffer, Q, K and V as
+    # views into it (token stride (Hq + 2 Hkv) d); scores, kept positions
+    # and the compacted cache equal those of separate contiguous tensors
+    _say(f"packed qkv a={a} b={b}")
+    bt = make_batch([23, 24], [1700, 600], 8, 2, 128, heavy=True)
+    q, k, v = to_device(bt)
+    qkv = torch.cat([q, k, v], dim=1).contiguous()
+    qv, kv_, vv = qkv[:, :8], qkv[:, 8:10], qkv[:, 10:12]
+    assert qv.stride(0) == 12 * 128 and kv_.stride() == vv.stride()
+    r1 = W.score_select_compact(q, k, v, bt.cu_seqlens, [a, a], [b, b], 128)
+    r2 = W.score_select_compact(qv, kv_, vv, bt.cu_seqlens, [a, a], [b, b], 128)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1), (0.01, 128)])
 def test_fp32_head_dim_128(a, b):
     # fp32 rows of 512 bytes take the row-group / key-group kernels
