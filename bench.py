@@ -206,11 +206,24 @@ KERNEL_SYMBOLS = {"pass1_lse": ("few_rows", "false"),
                   "pass2_colsum": ("few_rows", "true"),
                   "select_compact": ("select_kernel", "true")}
 
+# the same for the decode step (one kernel; the split merge is not counted)
+DECODE_SOURCES = ("attention_score_eviction_amd/csrc/decode.hpp",
+                  "attention_score_eviction_amd/csrc/decode_api.hip",
+                  "attention_score_eviction_amd/csrc/device_common.hpp")
+DECODE_SYMBOLS = {"decode": ("decode_kernel", None)}
 
-def kernel_source_hash() -> str:
+
+def _traffic_spec(workload_name: str):
+    """(kernel sources, bench kernel -> symbol match, description) of a workload's counter record."""
+    if workload_name == "decode":
+        return DECODE_SOURCES, DECODE_SYMBOLS, DECODE_WL["desc"]
+    return KERNEL_SOURCES, KERNEL_SYMBOLS, workload(workload_name)["desc"]
+
+
+def kernel_source_hash(workload_name: str = "8b") -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in _traffic_spec(workload_name)[0]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -226,7 +239,7 @@ def measured_traffic(kernel: str, workload_name: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(workload_name):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -279,9 +292,12 @@ def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
     cfetch/ and cwrite/ (the same over --copy-calibration copy_bytes), trace/
     (kernel trace).  The counters, in KiB per dispatch, are scaled by what
     they read for the copy, whose bytes are known."""
+    _, symbols, desc = _traffic_spec(workload_name)
+
     def pick(means, name):
-        base, flag = KERNEL_SYMBOLS[name]
-        hits = [k for k in means if base in k and (f", {flag}," in k or f", {flag}>" in k)]
+        base, flag = symbols[name]
+        hits = [k for k in means
+                if base in k and (flag is None or f", {flag}," in k or f", {flag}>" in k)]
         return max(hits, key=lambda k: means[k]) if hits else None
     fetch = _counter_means(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
     write = _counter_means(os.path.join(prof_dir, "write"), "WRITE_SIZE")
@@ -289,12 +305,12 @@ def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
     cwrite = max(_counter_means(os.path.join(prof_dir, "cwrite"), "WRITE_SIZE").values())
     trace = _trace_means(os.path.join(prof_dir, "trace"))
     ff, wf = copy_bytes / (cfetch * 1024.0), copy_bytes / (cwrite * 1024.0)
-    rec = {"workload": workload(workload_name)["desc"], "source_hash": kernel_source_hash(),
+    rec = {"workload": desc, "source_hash": kernel_source_hash(workload_name),
            "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
                                 "fetch_kib": cfetch, "write_kib": cwrite,
                                 "fetch_factor": ff, "write_factor": wf},
            "kernels": {}}
-    for name in KERNEL_SYMBOLS:
+    for name in symbols:
         sym = pick(fetch, name)
         if sym is None:
             continue
@@ -396,7 +412,7 @@ def decode_bench(args):
     roof = {"bound": "hbm", "kernel": "decode", "achieved": nbytes / (ms_kernel * 1e-3) / 1e9,
             "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic("decode", "decode")
     res = {
         "metric": "decode tokens/s over the compacted cache (one new token per sequence, one layer)",
         "value": bsz / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
