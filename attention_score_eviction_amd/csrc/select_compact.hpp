@@ -9,18 +9,22 @@
 // above T, then the lowest-positioned keys equal to T (ties go to the lower
 // position), are written in ascending position order.
 //
-// Layout: wave w owns the contiguous key segment [w * seg, (w + 1) * seg)
-// (seg a multiple of 64), lane l its keys w * seg + 64 i + l, so every load
-// is coalesced and position order is (wave, i, lane) order.  Segments of up
-// to 64 * PTC keys stay in registers across the passes; longer ones are
-// re-read (from L2) on every pass.
+// Layout: wave w owns the key segment [w * 64 PTC, (w + 1) * 64 PTC), lane l
+// its keys w * 64 PTC + 64 i + l (i < PTC), held in registers for the whole
+// select; every load is coalesced and position order is (wave, i, lane)
+// order.  Slots at or past N read as score 0.  They follow every real key in
+// position order, so they are never kept: a kept key equal to 0 is one of the
+// lowest-positioned zeros, and N > budget real keys come first.  That lets
+// every pass run over all slots with no bounds test.
 //
-// Histograms: the first digit is shared by almost every key, so its counts
-// go to per-(digit, lane % 32) words (the lanes of one atomic hit distinct
-// words instead of serialising on one) and are then folded into 256 digit
-// counts; later passes see few matching keys and count directly.  Every wave
-// derives the picked digit from the histogram itself: one barrier per pass
-// (two for the first).
+// Pass 1 (top byte, shared by almost every key): per-(digit, lane % 32)
+// counters keep the lanes of one atomic on distinct words, folded into 256
+// digit counts.  Pass 2 (second byte): branch-free, keys outside the top-byte
+// bucket count into a per-lane spare word.  Pass 3 (third byte): few keys
+// still match the 16-bit prefix P; the pass also counts the keys above P and
+// marks the (wave-uniform) slot indices holding keys in P, the only ones pass
+// 4 and the final counts visit.  Every wave derives the picked digit from
+// the histogram itself: one barrier per pass (two for the first).
 //
 // Output: a key's slot is (#kept keys above T before it) + min(#keys equal
 // to T before it, the number of T-equal keys kept), from wave ballots, their
@@ -29,7 +33,12 @@
 //
 // FUSE: the same workgroup then gathers the kept K and V rows (bit copies,
 // 16-byte vectors; zero rows past the kept count), so select and compact are
-// one launch.
+// one launch.  Once P is known (after pass 3), each lane requests into L2 the
+// K and V rows of one of its keys at or above P (kept, or still undecided):
+// plain loads whose values are consumed only after the gather, so pass 4,
+// the counts and the output run while they are in flight and the gather
+// finds most rows in L2.  A lane with several such keys (rare: about one key
+// in a hundred is kept) requests one of them.
 //
 // compact_kernel: one 16-byte vector per thread, rows of K and V copied bit
 // for bit; empty slots (-1) are zero-filled.
@@ -44,7 +53,6 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int SEL_SUB = 32;          // sub-counters per digit
 constexpr int SEL_FUSE_MAX = 8192;   // largest budget the fused gather keeps in LDS
-constexpr int SEL_BATCH = 16;        // keys per lane loaded together (no register cache)
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -79,8 +87,10 @@ __device__ __forceinline__ void pick_digit(const int* hist, int krem, int lane, 
 template <int PTC, bool FUSE>
 __global__ void __launch_bounds__(SEL_THREADS)
 select_kernel(const SelectArgs args) {
+  static_assert(PTC >= 1 && PTC <= 32, "slot marks are 32-bit masks");
   __shared__ __attribute__((aligned(16))) int sub[256 * SEL_SUB];
   __shared__ int hist[4][256];
+  __shared__ int spare[WAVE];
   __shared__ int wtot[2][SEL_WAVES];
   __shared__ int sel[FUSE ? SEL_FUSE_MAX : 1];
 
@@ -96,6 +106,12 @@ select_kernel(const SelectArgs args) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int32_t* out = args.idx + ((int64_t)p * args.hkv + h) * budget;
   for (int j = keep + tid; j < budget; j += SEL_THREADS) out[j] = -1;
+  const int vs = args.row_shift;
+  const int rb = 16 << vs;  // row bytes
+  const int64_t kbase = ((int64_t)tab.tok0[p] * args.st.kv_tok + (int64_t)h * args.st.kv_head) * args.elt;
+  const int64_t kv_row = args.st.kv_tok * args.elt;
+
+  uint32_t pfv[4] = {0u, 0u, 0u, 0u};  // L2 requests (values unused)
 
   if (keep == N) {  // every key is kept
     for (int j = tid; j < N; j += SEL_THREADS) {
@@ -104,16 +120,12 @@ select_kernel(const SelectArgs args) {
     }
   } else {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)h * args.T + tab.tok0[p]);
-    const int seg = (N + SEL_THREADS - 1) / SEL_THREADS * WAVE;  // keys per wave, multiple of 64
-    const int iters = seg / WAVE;
-    const int e0 = wave * seg + lane;
-    uint32_t cache[PTC > 0 ? PTC : 1];
-    if constexpr (PTC > 0) {
+    const int e0 = wave * (PTC * WAVE) + lane;  // slot i of this lane: key e0 + 64 i
+    uint32_t u[PTC];
 #pragma unroll
-      for (int i = 0; i < PTC; ++i) {
-        const int e = e0 + i * WAVE;
-        cache[i] = (i < iters && e < N) ? s[e] : 0u;
-      }
+    for (int i = 0; i < PTC; ++i) {
+      const int e = e0 + i * WAVE;
+      u[i] = e < N ? s[e] : 0u;
     }
     for (int i = tid; i < 256 * SEL_SUB / 4; i += SEL_THREADS)
       reinterpret_cast<int4*>(sub)[i] = int4{0, 0, 0, 0};
@@ -121,46 +133,11 @@ select_kernel(const SelectArgs args) {
     static_assert(SEL_THREADS == 4 * 256, "one histogram word per thread");
     __syncthreads();
 
-    // f(i, valid, bits) over this lane's keys, in position order.  `live`
-    // (wave-uniform) skips keys no lane still needs: bit i stands for the
-    // lane's i-th key with a register cache, for its i-th group of SEL_BATCH
-    // keys without one (all bits set past 64 groups).  Without a cache the
-    // keys are loaded SEL_BATCH at a time, all loads in flight together.
-    uint64_t live = ~0ull;
-    auto each_key = [&](auto&& f) {
-      if constexpr (PTC > 0) {
-#pragma unroll
-        for (int i = 0; i < PTC; ++i)
-          if (i < iters && ((live >> i) & 1u)) f(i, e0 + i * WAVE < N, cache[i]);  // wave-uniform
-      } else {
-        for (int i0 = 0; i0 < iters; i0 += SEL_BATCH) {
-          const int grp = i0 / SEL_BATCH;
-          if (grp < 64 && !((live >> grp) & 1u)) continue;  // wave-uniform
-          uint32_t c[SEL_BATCH];
-#pragma unroll
-          for (int i = 0; i < SEL_BATCH; ++i) {
-            const int e = e0 + (i0 + i) * WAVE;
-            c[i] = (i0 + i < iters && e < N) ? s[e] : 0u;
-          }
-#pragma unroll
-          for (int i = 0; i < SEL_BATCH; ++i)
-            if (i0 + i < iters) f(i0 + i, e0 + (i0 + i) * WAVE < N, c[i]);
-        }
-      }
-    };
-    // the `live` bit of the lane's i-th key
-    auto live_bit = [&](int i) -> uint64_t {
-      const int b = PTC > 0 ? i : i / SEL_BATCH;
-      return b < 64 ? 1ull << b : 0ull;
-    };
-
-    // pass 1 (top digit, shared by almost every key): per-(digit, lane % 32)
-    // counters keep the lanes of one atomic on distinct words
+    // pass 1: top byte
     {
       int* mysub = sub + (lane & (SEL_SUB - 1));
-      each_key([&](int, bool ok, uint32_t u) {
-        if (ok) atomicAdd(mysub + (u >> 24) * SEL_SUB, 1);
-      });
+#pragma unroll
+      for (int i = 0; i < PTC; ++i) atomicAdd(mysub + (u[i] >> 24) * SEL_SUB, 1);
       __syncthreads();
       const int d = tid >> 2, part = tid & 3;
       const int4* q4 = reinterpret_cast<const int4*>(sub + d * SEL_SUB + part * 8);
@@ -171,37 +148,75 @@ select_kernel(const SelectArgs args) {
     }
     int dgt, above;
     pick_digit(hist[0], keep, lane, dgt, above);
-    uint32_t prefix = (uint32_t)dgt << 24, pmask = 0xFF000000u;
     int krem = keep - above;
+    const uint32_t d1 = (uint32_t)dgt;
 
-    // passes 2-4: few keys still match, so plain atomics on one histogram
-    // per pass (cleared at the start: no clearing between passes)
+    // pass 2: second byte of the keys in the top-byte bucket
 #pragma unroll
-    for (int pass = 1; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      uint64_t nlive = iters > 64 * SEL_BATCH && PTC == 0 ? ~0ull : 0ull;
-      each_key([&](int i, bool ok, uint32_t u) {
-        const bool take = ok && (u & pmask) == prefix;
-        const uint64_t m = __ballot(take);
-        if (m != 0) nlive |= live_bit(i);
-        if (take) atomicAdd(&hist[pass][(u >> shift) & 255u], 1);
-      });
-      live = nlive;
-      __syncthreads();
-      pick_digit(hist[pass], krem, lane, dgt, above);
-      krem -= above;
-      prefix |= (uint32_t)dgt << shift;
-      pmask |= 255u << shift;
+    for (int i = 0; i < PTC; ++i) {
+      int* a = (u[i] >> 24) == d1 ? &hist[1][(u[i] >> 16) & 255u] : &spare[lane];
+      atomicAdd(a, 1);
     }
-    const uint32_t thr = prefix;
-    const int need_eq = krem;  // keys equal to thr that are kept (lowest positions)
-    live = ~0ull;
+    __syncthreads();
+    pick_digit(hist[1], krem, lane, dgt, above);
+    krem -= above;
+    const uint32_t P16 = (d1 << 8) | (uint32_t)dgt;
 
-    int n_gt = 0, n_eq = 0;  // wave totals (uniform)
-    each_key([&](int, bool ok, uint32_t u) {
-      n_gt += __builtin_popcountll(__ballot(ok && u > thr));
-      n_eq += __builtin_popcountll(__ballot(ok && u == thr));
-    });
+    // pass 3: third byte of the keys in P16; keys above P16 counted per lane
+    int n_hi = 0;
+    uint32_t cand = 0;  // bit i: slot i of some lane of this wave holds a key in P16
+    int pf = -1;        // a slot of this lane at or above P16
+#pragma unroll
+    for (int i = 0; i < PTC; ++i) {
+      const uint32_t t16 = u[i] >> 16;
+      n_hi += t16 > P16 ? 1 : 0;
+      if constexpr (FUSE) pf = t16 >= P16 ? i : pf;
+      const bool in = t16 == P16;
+      if (__ballot(in) != 0) {  // wave-uniform
+        cand |= 1u << i;
+        if (in) atomicAdd(&hist[2][(u[i] >> 8) & 255u], 1);
+      }
+    }
+    if constexpr (FUSE) {
+      // P16 > 0: slots past N (score 0) are below it, so pf names a real key
+      if (P16 != 0 && pf >= 0) {
+        const unsigned char* kr = args.k + kbase + (int64_t)(e0 + pf * WAVE) * kv_row;
+        const unsigned char* vr = args.v + kbase + (int64_t)(e0 + pf * WAVE) * kv_row;
+        const int second = rb > 128 ? 128 : 0;  // the row's second 128-byte line, if any
+        pfv[0] = *reinterpret_cast<const uint32_t*>(kr);
+        pfv[1] = *reinterpret_cast<const uint32_t*>(kr + second);
+        pfv[2] = *reinterpret_cast<const uint32_t*>(vr);
+        pfv[3] = *reinterpret_cast<const uint32_t*>(vr + second);
+      }
+    }
+    __syncthreads();
+    pick_digit(hist[2], krem, lane, dgt, above);
+    krem -= above;
+    const uint32_t P24 = (P16 << 8) | (uint32_t)dgt;
+
+    // pass 4: last byte, slots marked in pass 3 only
+#pragma unroll
+    for (int i = 0; i < PTC; ++i) {
+      if ((cand >> i) & 1u) {
+        if ((u[i] >> 8) == P24) atomicAdd(&hist[3][u[i] & 255u], 1);
+      }
+    }
+    __syncthreads();
+    pick_digit(hist[3], krem, lane, dgt, above);
+    krem -= above;
+    const uint32_t thr = (P24 << 8) | (uint32_t)dgt;
+    const int need_eq = krem;  // keys equal to thr that are kept (lowest positions)
+
+    // wave totals: keys above thr (above P16, or in P16 and above thr) and equal to thr
+    int n_gt = __builtin_amdgcn_readlane(wave_incl_scan(n_hi), WAVE - 1);
+    int n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < PTC; ++i) {
+      if ((cand >> i) & 1u) {
+        n_gt += __builtin_popcountll(__ballot((u[i] >> 16) == P16 && u[i] > thr));
+        n_eq += __builtin_popcountll(__ballot(u[i] == thr));
+      }
+    }
     if (lane == 0) {
       wtot[0][wave] = n_gt;
       wtot[1][wave] = n_eq;
@@ -212,10 +227,11 @@ select_kernel(const SelectArgs args) {
     int eb = wave_incl_scan(lane < wave ? wtot[1][lane] : 0);
     gb = __builtin_amdgcn_readlane(gb, SEL_WAVES - 1);
     eb = __builtin_amdgcn_readlane(eb, SEL_WAVES - 1);
-    each_key([&](int i, bool ok, uint32_t u) {
-      const bool gt = ok && u > thr, eq = ok && u == thr;
+#pragma unroll
+    for (int i = 0; i < PTC; ++i) {
+      if (__ballot(u[i] >= thr) == 0) continue;  // wave-uniform
+      const bool gt = u[i] > thr, eq = u[i] == thr;
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      if ((mg | me) == 0) return;  // wave-uniform
       const int g_before = gb + lanes_below(mg);
       const int e_before = eb + lanes_below(me);
       if (gt || (eq && e_before < need_eq)) {
@@ -226,27 +242,26 @@ select_kernel(const SelectArgs args) {
       }
       gb += __builtin_popcountll(mg);
       eb += __builtin_popcountll(me);
-    });
+    }
   }
 
   if constexpr (FUSE) {
     __syncthreads();
-    const int vs = args.row_shift;
-    const int rb = 16 << vs;  // row bytes
     const int total = budget << vs;
     const int64_t obase = ((int64_t)p * args.hkv + h) * budget * rb;
-    const int64_t kbase = ((int64_t)tab.tok0[p] * args.st.kv_tok + (int64_t)h * args.st.kv_head) * args.elt;
     for (int x = tid; x < total; x += SEL_THREADS) {
       const int j = x >> vs, c = x & ((1 << vs) - 1);
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (j < keep) {
-        const int64_t src = kbase + (int64_t)sel[j] * args.st.kv_tok * args.elt + c * 16;
+        const int64_t src = kbase + (int64_t)sel[j] * kv_row + c * 16;
         kv = ld16(args.k + src);
         vv = ld16(args.v + src);
       }
       st16(args.k_out + obase + (int64_t)j * rb + c * 16, kv);
       st16(args.v_out + obase + (int64_t)j * rb + c * 16, vv);
     }
+    // keeps the L2 requests alive; budget >= 1, so nothing is written
+    if (budget < 0) out[tid] = (int32_t)(pfv[0] ^ pfv[1] ^ pfv[2] ^ pfv[3]);
   }
 }
 

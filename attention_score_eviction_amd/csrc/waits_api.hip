@@ -682,12 +682,11 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
     fill_table(args.tab, v, lo, hi, s->n_kv_heads);
     const dim3 grid((hi - lo) * s->n_kv_heads);
+    static_assert(SEL_WIDE_MIN == SEL_THREADS * 32, "one workgroup holds at most 32 keys per lane");
     if (gmax <= SEL_THREADS * 16)
       hipLaunchKernelGGL((select_kernel<16, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
-    else if (gmax <= SEL_THREADS * 32)
-      hipLaunchKernelGGL((select_kernel<32, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
     else
-      hipLaunchKernelGGL((select_kernel<0, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+      hipLaunchKernelGGL((select_kernel<32, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
     if (launched() != WAITS_OK) return WAITS_EDEVICE;
   }
   return WAITS_OK;
