@@ -177,6 +177,7 @@ select_kernel(const SelectArgs args) {
         if (in) atomicAdd(&hist[2][(u[i] >> 8) & 255u], 1);
       }
     }
+    cand = __builtin_amdgcn_readfirstlane(cand);  // uniform: keeps the tests below scalar branches
     if constexpr (FUSE) {
       // P16 > 0: slots past N (score 0) are below it, so pf names a real key
       if (P16 != 0 && pf >= 0) {
@@ -198,6 +199,7 @@ select_kernel(const SelectArgs args) {
 #pragma unroll
     for (int i = 0; i < PTC; ++i) {
       if ((cand >> i) & 1u) {
+        asm volatile("");  // keeps this a scalar branch (not merged into the lane test below)
         if ((u[i] >> 8) == P24) atomicAdd(&hist[3][u[i] & 255u], 1);
       }
     }
@@ -213,6 +215,7 @@ select_kernel(const SelectArgs args) {
 #pragma unroll
     for (int i = 0; i < PTC; ++i) {
       if ((cand >> i) & 1u) {
+        asm volatile("");
         n_gt += __builtin_popcountll(__ballot((u[i] >> 16) == P16 && u[i] > thr));
         n_eq += __builtin_popcountll(__ballot(u[i] == thr));
       }
