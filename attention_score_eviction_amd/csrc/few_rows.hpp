@@ -367,12 +367,14 @@ few_rows_kernel(const FrArgs args) {
     csum = add_xor32(csum);
     if (hf == 0) red[j & (2 * FR_SUB - 1)][wave][col] = csum;
   };
+  // Run by the last wave, which holds no more row tiles than any other.
   auto flush = [&](int j) {
-    if (j >= 0 && j < nsub && tid < TILE) {
-      const int key = kbeg + j * TILE + tid;
+    const int ft = tid - (FR_THREADS - WAVE);  // lane of the last wave
+    if (j >= 0 && j < nsub && ft >= 0 && ft < TILE) {
+      const int key = kbeg + j * TILE + ft;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][tid];
+      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][ft];
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
     }
   };

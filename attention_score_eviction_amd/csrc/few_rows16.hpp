@@ -345,12 +345,15 @@ few_rows16_kernel(const FrArgs args) {
       if (g4 == 0) red[j & (2 * FR_SUB - 1)][wave][kt * T16 + c16] = sv;
     }
   };
+  // Run by the last wave: waves with higher indices hold no more tiles than
+  // lower ones, so the last SIMD (waves 3 and 7) carries the fewest tiles.
   auto flush = [&](int j) __attribute__((always_inline)) {
-    if (j >= 0 && j < nsub && tid < TILE) {
-      const int key = kbeg + j * TILE + tid;
+    const int ft = tid - (FR_THREADS - WAVE);  // lane of the last wave
+    if (j >= 0 && j < nsub && ft >= 0 && ft < TILE) {
+      const int key = kbeg + j * TILE + ft;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][tid];
+      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][ft];
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
     }
   };

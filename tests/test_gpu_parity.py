@@ -381,6 +381,31 @@ def test_select_segment_boundaries(n):
             np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
 
 
+@pytest.mark.parametrize("n", [129, 1000, 5000, 16383, 20001, 32767])
+def test_select_threshold_zero(n):
+    # fewer positive scores than the budget: the kept zeros are the
+    # lowest-positioned ones (the kernel's slots past N also read as 0 and
+    # must never be kept); one head all zeros, one with 40 positives
+    _say(f"select threshold 0 n={n}")
+    rng = np.random.default_rng(2000 + n)
+    s = np.zeros((2, n), dtype=np.float32)
+    s[1, rng.choice(n, 40, replace=False)] = rng.random(40).astype(np.float32) + np.float32(0.5)
+    sd = torch.from_numpy(s).to(DEV)
+    idx = W.select(sd, [0, n], 128).cpu().numpy()
+    for h in range(2):
+        np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), 128))
+    assert idx[0, 0].tolist() == list(range(128))
+    # the fused gather keeps the same rows, bit for bit
+    k = torch.randn((n, 2, 64), device=DEV).to(torch.bfloat16)
+    v = torch.randn((n, 2, 64), device=DEV).to(torch.bfloat16)
+    idx2, kc, vc = W.select_compact(sd, k, v, [0, n], 128)
+    assert np.array_equal(idx2.cpu().numpy(), idx)
+    for h in range(2):
+        rows = torch.from_numpy(idx[0, h].astype(np.int64)).to(DEV)
+        assert torch.equal(kc[0, h].view(torch.int16), k[rows, h].view(torch.int16))
+        assert torch.equal(vc[0, h].view(torch.int16), v[rows, h].view(torch.int16))
+
+
 @pytest.mark.parametrize("lengths,budget", [([3000, 17000, 40, 0, 33000], 256), ([5000, 9000], 10000),
                                             ([700] * 40, 64), ([128, 127, 129], 128)])
 def test_select_compact_fused_matches_separate(lengths, budget):
