@@ -80,7 +80,7 @@ few_rows_kernel(const FrArgs args) {
   __shared__ __attribute__((aligned(16))) int row_q[ROWS];       // row position (-1: padding)
   // pass 2: per-wave key sums of a sub-tile; 2 FR_SUB slots, so one stage's
   // stores never meet the previous stage's flushes
-  __shared__ float red[2 * FR_SUB][FR_WAVES][TILE];
+  __shared__ __attribute__((aligned(16))) float red[2 * FR_SUB][FR_WAVES][2 * TILE];  // key k: [2k], [2k + 1]
 
   const SeqTable& tab = args.tab;
   const int item = blockIdx.x;
@@ -363,10 +363,8 @@ few_rows_kernel(const FrArgs args) {
     }
   };
   // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)
-  auto red_store = [&](int j, float csum) {
-    csum = add_xor32(csum);
-    if (hf == 0) red[j & (2 * FR_SUB - 1)][wave][col] = csum;
-  };
+  // each lane half stores its own rows' sum; the flush adds the two halves
+  auto red_store = [&](int j, float csum) { red[j & (2 * FR_SUB - 1)][wave][2 * col + hf] = csum; };
   // Run by the last wave, which holds no more row tiles than any other.
   auto flush = [&](int j) {
     const int ft = tid - (FR_THREADS - WAVE);  // lane of the last wave
@@ -374,7 +372,10 @@ few_rows_kernel(const FrArgs args) {
       const int key = kbeg + j * TILE + ft;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][ft];
+      for (int w = 0; w < FR_WAVES; ++w) {
+        const float2 hv = *reinterpret_cast<const float2*>(&red[j & (2 * FR_SUB - 1)][w][2 * ft]);
+        sc += hv.x + hv.y;
+      }
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
     }
   };

@@ -59,7 +59,7 @@ few_rows16_kernel(const FrArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float row_off[ROWS];
   __shared__ __attribute__((aligned(16))) int row_q[ROWS];
-  __shared__ float red[2 * FR_SUB][FR_WAVES][TILE];
+  __shared__ __attribute__((aligned(16))) float red[2 * FR_SUB][FR_WAVES][2 * TILE];  // key k: [2k], [2k + 1]
 
   const SeqTable& tab = args.tab;
   const int item = blockIdx.x;
@@ -337,13 +337,16 @@ few_rows16_kernel(const FrArgs args) {
     if constexpr (!PASS2) p1_commit(par, ln, live, diag_any, ktj, ntv_c);
   };
 
-  // pass 2: key sums of sub-tile j -> LDS slot (fixed-order cross-wave sum in flush)
+  // pass 2: key sums of sub-tile j -> LDS slot (fixed-order cross-wave sum in flush).
+  // One v_permlane16_swap of the two key tiles' sums (odd 16-lane rows of the
+  // first with even rows of the second) leaves lane group g4 with key tile
+  // g4 & 1's sum over lane groups 2 (g4 >> 1) and 2 (g4 >> 1) + 1; every lane
+  // stores it as half g4 >> 1 of its key, and the flush adds the two halves.
   auto red_store = [&](int j, const float* csum) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const float sv = add_xor32(add_xor16(csum[kt]));
-      if (g4 == 0) red[j & (2 * FR_SUB - 1)][wave][kt * T16 + c16] = sv;
-    }
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(csum[0]), __float_as_uint(csum[1]), false,
+                                                    false);
+    const float hs = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    red[j & (2 * FR_SUB - 1)][wave][2 * ((g4 & 1) * T16 + c16) + (g4 >> 1)] = hs;
   };
   // Run by the last wave: waves with higher indices hold no more tiles than
   // lower ones, so the last SIMD (waves 3 and 7) carries the fewest tiles.
@@ -353,7 +356,10 @@ few_rows16_kernel(const FrArgs args) {
       const int key = kbeg + j * TILE + ft;
       float sc = 0.f;
 #pragma unroll
-      for (int w = 0; w < FR_WAVES; ++w) sc += red[j & (2 * FR_SUB - 1)][w][ft];
+      for (int w = 0; w < FR_WAVES; ++w) {
+        const float2 hv = *reinterpret_cast<const float2*>(&red[j & (2 * FR_SUB - 1)][w][2 * ft]);
+        sc += hv.x + hv.y;
+      }
       if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
     }
   };
