@@ -257,7 +257,8 @@ few_rows_kernel(const FrArgs args) {
     bool ok = true;
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) ok = ok && (!live[t] || ln[t] < 0x1p64f);
-    if (__builtin_expect(ok, 1)) {
+    // wave-uniform: the compiler keeps the rare path's set-up out of the hot block
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) == 0, 1)) {
 #pragma unroll
       for (int t = 0; t < FR_TW; ++t)
         if (live[t]) lsum[t] = ln[t];
