@@ -47,6 +47,8 @@ struct FrArgs {
   float* lse;                 // pass 1 out (single chunk) / pass 2 in: [Hq, T]
   float2* part;               // pass 1 partials when a head's keys are split
   float* scores;              // pass 2 out: [Hkv, T]
+  float* cpart;               // pass 2 of heads in several row blocks: each block's column
+                              // sums, [ws0 + (row block * hkv + h) * N + key] (keys the block sees)
   Strides st;
   int64_t T;
   int32_t G;
@@ -97,10 +99,12 @@ few_rows_kernel(const FrArgs args) {
   const int64_t tok0 = tab.tok0[p];
   const int rbase = rb * ROWS;                // first packed row of the block
   const int qb0 = q0 + rbase / G;             // its first query
-  // Keys: pass 2 (one row block) the sequence's keys in chunks of kc; pass 1
-  // the keys up to the block's last query, cut into nc chunks.
+  // Keys: pass 2 of a head in one row block, the sequence's keys in chunks of
+  // kc; otherwise (pass 1, and pass 2 of a head in several row blocks) the
+  // keys up to the block's last query, cut into nc chunks.
+  const bool blocks = tab.nrb[p] > 1;
   int kbeg, kend;
-  if constexpr (PASS2) {
+  if (PASS2 && !blocks) {
     kbeg = chunk * tab.kc[p];
     kend = min(kbeg + tab.kc[p], N);
   } else {
@@ -119,13 +123,13 @@ few_rows_kernel(const FrArgs args) {
   const unsigned char* kb = static_cast<const unsigned char*>(args.k);
   const float cl2 = args.scale_log2;
 
-  if constexpr (!PASS2) {
-    if (kbeg >= kend) {  // a chunk past the block's keys: its partials are empty
+  if (kbeg >= kend) {  // a chunk past the block's keys
+    if constexpr (!PASS2) {  // its pass-1 partials are empty
       for (int r = tid; r < ROWS && rbase + r < PR; r += FR_THREADS)
         args.part[tab.ws0[p] + ((int64_t)h * tab.prow[p] + rbase + r) * nc + chunk] =
             make_float2(-INFINITY, 0.f);
-      return;
     }
+    return;  // pass 2: the reduce reads no key of this range for this block
   }
 
   // Row table (and pass-2 exponent offsets): one thread per packed row.
@@ -377,7 +381,10 @@ few_rows_kernel(const FrArgs args) {
         const float2 hv = *reinterpret_cast<const float2*>(&red[j & (2 * FR_SUB - 1)][w][2 * ft]);
         sc += hv.x + hv.y;
       }
-      if (key < kend) args.scores[(int64_t)h * args.T + tok0 + key] = sc;
+      if (key < kend) {
+        if (blocks) args.cpart[tab.ws0[p] + ((int64_t)rb * hkv + h) * N + key] = sc;
+        else args.scores[(int64_t)h * args.T + tok0 + key] = sc;
+      }
     }
   };
 
@@ -483,6 +490,40 @@ few_rows_kernel(const FrArgs args) {
       }
     }
   }
+}
+
+// Pass 2 of heads in several row blocks: a key's score is the sum, in
+// row-block order, of the column sums of the blocks whose rows can see it.
+// Block rb sees key k when G (k - q0) is at most its last packed row, i.e.
+// from block floor(G max(0, k - q0) / rows) on (the last block sees every key).
+struct RowBlockReduceArgs {
+  const float* cpart;
+  float* scores;
+  int64_t T;
+  int32_t hkv;
+  int32_t G;
+  int32_t rows;               // packed rows per block
+  SeqTable tab;               // first[]: items (hkv * N per sequence); nrb, n, q0, ws0, tok0
+};
+
+__global__ void __launch_bounds__(256)
+rowblock_reduce_kernel(const RowBlockReduceArgs args) {
+  const SeqTable& tab = args.tab;
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= tab.first[tab.nb]) return;
+  const int p = find_seq(tab.first, tab.nb, item);
+  const int local = item - tab.first[p];
+  const int N = tab.n[p];
+  const int h = local / N;
+  const int key = local - h * N;
+  const int nrb = tab.nrb[p];
+  const int64_t R = (int64_t)args.G * max(0, key - tab.q0[p]);
+  const int rb0 = (int)min<int64_t>(R / args.rows, nrb - 1);
+  const float* src = args.cpart + tab.ws0[p] + (int64_t)h * N + key;
+  const int64_t stride = (int64_t)args.hkv * N;
+  float sum = 0.f;
+  for (int rb = rb0; rb < nrb; ++rb) sum += src[rb * stride];
+  args.scores[(int64_t)h * args.T + tab.tok0[p] + key] = sum;
 }
 
 }  // namespace waits

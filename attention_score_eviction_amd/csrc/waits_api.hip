@@ -38,6 +38,8 @@ constexpr int KB_MIN_ROWS = 256;                  // key blocks: fewest rows per
 constexpr int KB_MAX_CHUNKS = 64;                 // key blocks: most row chunks
 constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chunk (< 2^31)
 constexpr int SEL_WIDE_MIN = SEL_THREADS * 32;    // longer key ranges: select over several workgroups
+constexpr int64_t RB_PART_MAX = int64_t(1) << 30;        // BIG pass 2 in row blocks: one sequence's partials
+constexpr int64_t RB_PART_TOTAL = int64_t(2) << 30;      // ... and one launch group's
 
 // Few-rows workgroup shapes: a head takes the smallest that holds its packed
 // rows (row blocks of longer heads use the largest).  tiles: 32-row tiles per
@@ -59,7 +61,8 @@ static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the large
 enum class Mode {
   NONE,   // no tokens
   FR,     // all packed rows of a KV head in one workgroup: few-rows kernel, both passes
-  BIG,    // more rows: pass 1 on the few-rows kernel in row blocks, pass 2 on key blocks
+  BIG,    // more rows: pass 1 on the few-rows kernel in row blocks; pass 2 on the same row blocks
+          // (reduced in block order), or on key blocks for the longest heads
   WIDE,   // fp32 rows of head_dim 128 (too wide for those register budgets): lse/colsum kernels
 };
 
@@ -71,6 +74,7 @@ struct Seq {
   int nrb = 0;                // FR / BIG pass 1: row blocks of that shape's rows
   int nkb = 0;                // BIG pass 2: key blocks of KB_KEYS keys
   int nrc = 1;                // BIG pass 2: row chunks per key block
+  bool p2rb = false;          // BIG pass 2 in row blocks (few-rows kernel) instead of key blocks
   int nc = 1, kc = 32;        // key chunks: pass 1 (every mode), pass 2 (FR)
   int64_t tok0 = 0;
   float a = 0.f, c = 0.f;
@@ -149,8 +153,12 @@ int64_t group_span(const waits_shape* s) {
 // Launch plan.  A sequence whose packed rows fit one workgroup per KV head
 // runs both passes on the few-rows kernel, its key range cut into chunks
 // until the batch has about one workgroup per compute unit.  A longer one
-// runs pass 1 on the same kernel in row blocks (key chunks for balance) and
-// pass 2 on key blocks (row chunks for balance).  Every chunk a buffer load
+// runs pass 1 on the same kernel in row blocks (key chunks for balance).  Its
+// pass 2 runs on the same row blocks and key chunks, each block writing its
+// column sums for a fixed-order reduce, while the partials stay under
+// RB_PART_MAX per sequence and RB_PART_TOTAL per launch group; other long
+// sequences run pass 2 on key blocks (row chunks for balance), whose partials
+// are [row chunk][Hkv][T].  Every chunk a buffer load
 // addresses spans less than 2^31 bytes.
 std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b) {
   const int G = s->n_q_heads / s->n_kv_heads;
@@ -221,6 +229,20 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       q.nc = (q.n + q.kc - 1) / q.kc;
     }
   }
+  // BIG pass 2 on the pass-1 row blocks and key chunks, each block writing its
+  // column sums for a reduce in block order, while the partials stay small
+  // (per sequence, and summed over a launch group, in sequence order); the
+  // other BIG sequences run pass 2 on key blocks.
+  for (int lo = 0; lo < s->batch; lo += MAXB) {
+    int64_t total = 0;
+    for (int i = lo; i < std::min(s->batch, lo + MAXB); ++i) {
+      Seq& q = v[i];
+      if (q.mode != Mode::BIG) continue;
+      const int64_t bytes = (int64_t)q.nrb * hkv * q.n * (int64_t)sizeof(float);
+      q.p2rb = bytes <= RB_PART_MAX && total + bytes <= RB_PART_TOTAL;
+      if (q.p2rb) total += bytes;
+    }
+  }
   return v;
 }
 
@@ -244,12 +266,29 @@ size_t lse_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
   return (size_t)mx * sizeof(float2);
 }
 
-// Pass-2 partial sums: [row chunk][Hkv][T] fp32 for the most-split sequence.
-size_t colsum_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+// Pass-2 partial sums.  Key blocks: [row chunk][Hkv][T] fp32 for the
+// most-split sequence.  Then, from a 256-byte boundary, row blocks: per
+// launch group, [row block][Hkv][N] fp32 per sequence, back to back.
+size_t kb_part_bytes(const waits_shape* s, const std::vector<Seq>& v) {
   int mx = 0;
   for (const Seq& q : v)
-    if (q.mode == Mode::BIG && q.nrc > 1) mx = std::max(mx, q.nrc);
-  return (size_t)mx * s->n_kv_heads * (size_t)s->cu_seqlens[s->batch] * sizeof(float);
+    if (q.mode == Mode::BIG && !q.p2rb && q.nrc > 1) mx = std::max(mx, q.nrc);
+  const size_t bytes = (size_t)mx * s->n_kv_heads * (size_t)s->cu_seqlens[s->batch] * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int64_t rb_part_floats(const std::vector<Seq>& v, int lo, int hi, int hkv) {
+  int64_t n = 0;
+  for (int i = lo; i < hi; ++i)
+    if (v[i].mode == Mode::BIG && v[i].p2rb) n += (int64_t)v[i].nrb * hkv * v[i].n;
+  return n;
+}
+
+size_t colsum_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+  int64_t rb = 0;
+  for (int lo = 0; lo < s->batch; lo += MAXB)
+    rb = std::max(rb, rb_part_floats(v, lo, std::min(s->batch, lo + MAXB), s->n_kv_heads));
+  return kb_part_bytes(s, v) + (size_t)rb * sizeof(float);
 }
 
 size_t lse_buffer_bytes(const waits_shape* s) {
@@ -458,25 +497,56 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
   if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 4)))) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;
   const int hkv = s->n_kv_heads;
+  float* cpart = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kb_part_bytes(s, v));
   for (int lo = 0; lo < s->batch; lo += MAXB) {
     const int hi = std::min(s->batch, lo + MAXB);
     SeqTable tab;
     fill_table(tab, v, lo, hi, hkv);
+    // row-block partials of this launch group, sequence by sequence
+    SeqTable rbtab = tab;
+    int64_t rb_off = 0;
+    for (int i = lo; i < hi; ++i) {
+      rbtab.ws0[i - lo] = rb_off;
+      if (v[i].mode == Mode::BIG && v[i].p2rb) rb_off += (int64_t)v[i].nrb * hkv * v[i].n;
+    }
 
-    // few-rows sequences: one launch per workgroup shape
+    // few-rows sequences, and the row blocks of longer ones: one launch per workgroup shape
     for (int shape = 0; shape < FR_NSHAPES; ++shape) {
       FrArgs f = fr_args(s, q, k);
       f.lse = const_cast<float*>(lse);
       f.scores = scores;
-      f.tab = tab;
+      f.cpart = cpart;
+      f.tab = rbtab;
       int fr_items = 0;
       for (int i = lo; i < hi; ++i) {
         f.tab.first[i - lo] = fr_items;
-        if (v[i].mode == Mode::FR && v[i].frs == shape) fr_items += hkv * v[i].nc;
+        if (v[i].frs != shape) continue;
+        if (v[i].mode == Mode::FR) fr_items += hkv * v[i].nc;
+        else if (v[i].mode == Mode::BIG && v[i].p2rb) fr_items += hkv * v[i].nrb * v[i].nc;
       }
       f.tab.first[hi - lo] = fr_items;
       if (fr_items > 0) {
         dispatch_fr<true>(s, f, fr_items, shape, stream);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+      }
+    }
+    {
+      RowBlockReduceArgs ra;
+      ra.cpart = cpart;
+      ra.scores = scores;
+      ra.T = s->cu_seqlens[s->batch];
+      ra.hkv = hkv;
+      ra.G = G;
+      ra.rows = FR_ROWS;
+      ra.tab = rbtab;
+      int items = 0;
+      for (int i = lo; i < hi; ++i) {
+        ra.tab.first[i - lo] = items;
+        if (v[i].mode == Mode::BIG && v[i].p2rb) items += hkv * v[i].n;
+      }
+      ra.tab.first[hi - lo] = items;
+      if (items > 0) {
+        hipLaunchKernelGGL(rowblock_reduce_kernel, dim3((items + 255) / 256), dim3(256), 0, stream, ra);
         if (launched() != WAITS_OK) return WAITS_EDEVICE;
       }
     }
@@ -506,7 +576,7 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
       kbargs.tab.nc[i - lo] = v[i].nrc;
       rargs.tab.first[i - lo] = red_items;
       rargs.tab.nc[i - lo] = v[i].nrc;
-      if (v[i].mode == Mode::BIG) {
+      if (v[i].mode == Mode::BIG && !v[i].p2rb) {
         kb_items += hkv * v[i].nkb * v[i].nrc;
         if (v[i].nrc > 1) red_items += hkv * v[i].n;
       }

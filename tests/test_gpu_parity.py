@@ -129,6 +129,29 @@ def test_long_context_h2o_sampled(long_prompt):
     check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, bt.cu_seqlens)
 
 
+def test_row_block_and_key_block_pass2_in_one_launch():
+    # a=0 everywhere: the 70000-token prompt's row-block partials (547 blocks x
+    # 8 heads x 70000 keys, 1.2 GB) exceed the per-sequence cap, so its pass 2
+    # runs on key blocks; the 1500-token prompt's runs on row blocks with a
+    # block-order reduce.  Both share one launch group and one workspace.
+    _say("pass 2 on key blocks and row blocks in one batch")
+    lens = [70000, 1500]
+    bt = make_batch([91, 92], lens, 32, 8, 128, heavy=True)
+    s_gpu, idx, kc, vc = _run_all(bt, [0.0, 0.0], [1, 1], 256)
+    cu = bt.cu_seqlens
+    tail = lens[0] - 48
+    s_ref = orc.waits_scores(bt.q, bt.k, cu, 32, 8, [0.0, 0.0], [1, 1],
+                             float(np.float32(1 / math.sqrt(128))), row_min=[tail, 0])
+    # the long prompt: exact on its last 48 keys (they see only the last 48
+    # rows) and the mass invariant sum_k s[h, k] = G * N / 2 on every head
+    check_scores(s_gpu[:, tail:lens[0]], s_ref[:, tail:lens[0]])
+    np.testing.assert_allclose(s_gpu[:, :lens[0]].astype(np.float64).sum(axis=1), 2.0 * lens[0], rtol=1e-4)
+    # the short prompt: every key
+    check_scores(s_gpu[:, lens[0]:], s_ref[:, lens[0]:])
+    check_select_exact(idx, s_gpu, cu, 256)
+    check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, cu)
+
+
 @pytest.fixture(scope="module")
 def longest_prompt():
     return make_prompt(9, (1 << 22) - 1, 1, 1, 64, heavy=True, dtype="bf16")
