@@ -1,9 +1,10 @@
 // Both QK^T passes for sequences whose processed rows are few: when the G
 // query heads of a KV head have at most FR_ROWS packed rows in total (large
 // a: only the last rows carry weight), one workgroup holds every row of the
-// head in registers and streams K past them exactly once.  Pass 1 also runs
-// here for heads with more rows, one block of FR_ROWS packed rows per
-// workgroup (the block's keys end at its last query).
+// head in registers and streams K past them exactly once.  Heads with more
+// rows run here too, one block of FR_ROWS packed rows per workgroup (the
+// block's keys end at its last query): pass 1 always, pass 2 while the
+// blocks' partial column sums fit the workspace limits of the host plan.
 //
 // Work item = (sequence, KV head h, row block, key chunk).  8 waves; wave w owns packed
 // row tiles w and w + 8 (32 rows each, MFMA operand fragments in
@@ -26,11 +27,12 @@
 // Pass 2 (weighted column sums).  MFMA(A = Q rows, B = K tile): each lane
 // owns one key and 16 rows per tile; p = exp2(dot * scale*log2 e - off[row])
 // with off = lse * log2 e + log2(1 + exp(-a (q - c))) (w folded in, off =
-// +inf for rows whose fp32 weight is 0).  A tile's 32 key scores are complete
-// inside the workgroup (every row of the head is here): in-lane sums, one
-// exchange between lane halves, and an 8-wave sum through LDS in a fixed
-// order, written straight to the score array -- no partial buffers, no
-// atomics, bitwise reproducible.
+// +inf for rows whose fp32 weight is 0).  In-lane sums, then each lane half
+// stores its rows' sum to LDS and the last wave adds the two halves of every
+// wave in a fixed order.  A head in one block has every row here, so that
+// sum is the score, written straight to the score array; a head in several
+// blocks writes it as the block's partial (cpart), and rowblock_reduce_kernel
+// adds the blocks in order -- no atomics, bitwise reproducible.
 #pragma once
 
 #include "device_common.hpp"
