@@ -31,6 +31,10 @@ def compile_command(out: str) -> list:
         _hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # no packed fp32 VALU instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # instruction-level-parallelism scheduling: the QK^T passes' MFMA and
+        # exponential streams interleave better (the headline step measured
+        # 2.3% faster, outputs bit-identical; no kernel spills or loses occupancy)
+        "-mllvm", "-amdgpu-sched-strategy=max-ilp",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
         os.path.join(CSRC, "waits_api.hip"), os.path.join(CSRC, "decode_api.hip"), "-o", out,

@@ -192,7 +192,8 @@ def cpu_baseline(wl, budget_s: float):
                       f"{len(os.sched_getaffinity(0))} cpus in affinity; {cpu}"}
 
 
-KERNEL_SOURCES = ("attention_score_eviction_amd/csrc/few_rows.hpp",
+KERNEL_SOURCES = ("attention_score_eviction_amd/build.py",  # compile flags shape the kernels too
+                  "attention_score_eviction_amd/csrc/few_rows.hpp",
                   "attention_score_eviction_amd/csrc/few_rows16.hpp",
                   "attention_score_eviction_amd/csrc/key_blocks.hpp",
                   "attention_score_eviction_amd/csrc/select_compact.hpp",
@@ -207,7 +208,8 @@ KERNEL_SYMBOLS = {"pass1_lse": ("few_rows", "false"),
                   "select_compact": ("select_kernel", "true")}
 
 # the same for the decode step (one kernel; the split merge is not counted)
-DECODE_SOURCES = ("attention_score_eviction_amd/csrc/decode.hpp",
+DECODE_SOURCES = ("attention_score_eviction_amd/build.py",
+                  "attention_score_eviction_amd/csrc/decode.hpp",
                   "attention_score_eviction_amd/csrc/decode_api.hip",
                   "attention_score_eviction_amd/csrc/device_common.hpp")
 DECODE_SYMBOLS = {"decode": ("decode_kernel", None)}
