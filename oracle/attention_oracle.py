@@ -11,7 +11,7 @@ prompt row; the softmax normaliser of each row is what WAITS pass 1 needs.
 The attention itself is the model's ordinary causal scaled dot-product
 attention.
 
-Readings taken where the page is silent (each is also listed in the design doc):
+Readings taken where the page is silent:
 
 * ``out[t0 + q, g] = sum_{k <= q} softmax_k(scale <Q[q, g], K[k, h]>) V[k, h]``
   for every query row ``q`` of every prompt (0-based positions restarting per

@@ -9,7 +9,7 @@ selected key-value pairs; its "Quickstart" compresses the cache with
 ``init_cache`` and then generates, so every decoding step attends over the
 kept rows (and the rows generation appends after them).
 
-Readings taken where the page is silent (each is also listed in the design doc):
+Readings taken where the page is silent:
 
 * the attention of a decoding step is the model's ordinary scaled
   dot-product attention: for query head ``g`` of sequence ``i``,

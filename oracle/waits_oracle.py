@@ -11,7 +11,7 @@ The README's "Quickstart" names the knobs (``sigmoid_a`` = a,
 ``recent_budget`` = b, ``select_budget`` = number of keys kept) and its
 "Repository layout" names the selector (top-k).
 
-Readings taken where the page is silent (each is also listed in the design doc):
+Readings taken where the page is silent:
 
 * query and key positions are 0-based (with b = 1 and a -> inf only the last
   row keeps weight, which is the TOVA limit the introduction names);
