@@ -102,6 +102,7 @@ int check_shape(const waits_shape* s, bool need_q) {
     if (s->q_stride_tok < 0 || s->q_stride_head < 0) return WAITS_EINVAL;
     if ((s->q_stride_tok * e) % 16 || (s->q_stride_head * e) % 16) return WAITS_EINVAL;
     if (!(std::isfinite(s->scale) && s->scale > 0.f)) return WAITS_EINVAL;
+    if (s->pass2 != WAITS_PASS2_AUTO && s->pass2 != WAITS_PASS2_KEY_BLOCKS) return WAITS_EINVAL;
   }
   return WAITS_OK;
 }
@@ -217,7 +218,10 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       const int64_t want2 = std::max<int64_t>(1, ceil_div(8 * NUM_CU, big_units2));
       int64_t nrc = std::min<int64_t>({want2, KB_MAX_CHUNKS, ceil_div(q.pr, KB_MIN_ROWS)});
       nrc = std::max<int64_t>(1, nrc);
-      q.nrc = (int)std::max(nrc, ceil_div((q.n - q.q0 + 1) * qrow, SPAN_BYTES - group_span(s)));
+      // each chunk's Q rows span less than 2^30 bytes (wider groups are refused in run_colsum)
+      const int64_t room = SPAN_BYTES - group_span(s);
+      if (room > 0) nrc = std::max(nrc, ceil_div((q.n - q.q0 + 1) * qrow, room));
+      q.nrc = (int)nrc;
     }
   }
   if (wide_rg > 0 && wide_rg < 2 * NUM_CU) {
@@ -232,8 +236,10 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
   // BIG pass 2 on the pass-1 row blocks and key chunks, each block writing its
   // column sums for a reduce in block order, while the partials stay small
   // (per sequence, and summed over a launch group, in sequence order); the
-  // other BIG sequences run pass 2 on key blocks.
-  for (int lo = 0; lo < s->batch; lo += MAXB) {
+  // other BIG sequences run pass 2 on key blocks, and so do all of them when
+  // the caller asks for the key-block plan.
+  const bool rb_ok = s->pass2 == WAITS_PASS2_AUTO;
+  for (int lo = 0; rb_ok && lo < s->batch; lo += MAXB) {
     int64_t total = 0;
     for (int i = lo; i < std::min(s->batch, lo + MAXB); ++i) {
       Seq& q = v[i];
@@ -491,8 +497,9 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
                const float* a, const int32_t* b, float* scores, void* ws, size_t ws_bytes,
                hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, a, b);
+  // only the key-block kernel addresses a group's Q rows from one buffer base
   for (const Seq& sq : v)
-    if (sq.mode == Mode::BIG && group_span(s) > SPAN_BYTES / 2) return WAITS_EUNSUPPORTED;
+    if (sq.mode == Mode::BIG && !sq.p2rb && group_span(s) > SPAN_BYTES / 2) return WAITS_EUNSUPPORTED;
   const size_t need = colsum_ws_bytes(s, v);
   if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 4)))) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;

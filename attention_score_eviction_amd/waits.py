@@ -30,6 +30,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "waits.h")
 
 WAITS_OK, WAITS_EINVAL, WAITS_EUNSUPPORTED, WAITS_EWORKSPACE, WAITS_EDEVICE = range(5)
 WAITS_BF16, WAITS_F32 = 0, 1
+WAITS_PASS2_AUTO, WAITS_PASS2_KEY_BLOCKS = 0, 1
+_PASS2 = {"auto": WAITS_PASS2_AUTO, "key_blocks": WAITS_PASS2_KEY_BLOCKS}
 
 
 class WaitsError(RuntimeError):
@@ -51,6 +53,7 @@ class WaitsShape(ctypes.Structure):
         ("kv_stride_tok", ctypes.c_int64),
         ("kv_stride_head", ctypes.c_int64),
         ("scale", ctypes.c_float),
+        ("pass2", ctypes.c_int32),
     ]
 
 
@@ -137,7 +140,8 @@ class _Marshal:
     """Host-side argument block for one call (keeps the host arrays alive)."""
 
     def __init__(self, cu_seqlens, q: Optional[torch.Tensor], kv: torch.Tensor,
-                 scale: Optional[float], a=None, b=None, n_q_heads: Optional[int] = None):
+                 scale: Optional[float], a=None, b=None, n_q_heads: Optional[int] = None,
+                 pass2: str = "auto"):
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
         batch = len(self.cu) - 1
         if kv.dtype == torch.bfloat16:
@@ -162,6 +166,9 @@ class _Marshal:
         if scale is None:
             scale = 1.0 / math.sqrt(d)
         self.shape.scale = float(scale)
+        if pass2 not in _PASS2:
+            raise ValueError(f"pass2 must be one of {sorted(_PASS2)}, got {pass2!r}")
+        self.shape.pass2 = _PASS2[pass2]
         self.a = self.b = None
         if a is not None:
             self.a = np.ascontiguousarray(np.broadcast_to(np.asarray(a, np.float32), (batch,)))
@@ -202,24 +209,24 @@ def first_rows(cu_seqlens, a, b) -> np.ndarray:
     return out
 
 
-def lse_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
-    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+def lse_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     out = ctypes.c_size_t(0)
     _check("waits_lse_workspace_bytes",
            lib().waits_lse_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
     return out.value
 
 
-def colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
-    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+def colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     out = ctypes.c_size_t(0)
     _check("waits_colsum_workspace_bytes",
            lib().waits_colsum_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
     return out.value
 
 
-def score_workspace_bytes(q, k, cu_seqlens, a, b, scale=None) -> int:
-    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+def score_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
+    m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     out = ctypes.c_size_t(0)
     _check("waits_score_workspace_bytes",
            lib().waits_score_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
@@ -254,13 +261,14 @@ def lse(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
 
 def colsum(q: torch.Tensor, k: torch.Tensor, lse_rows: torch.Tensor, cu_seqlens, a, b,
            scale=None, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Pass 2: WAITS key scores [Hkv, T] fp32 from the pass-1 normalisers."""
+           workspace: Optional[torch.Tensor] = None, pass2: str = "auto") -> torch.Tensor:
+    """Pass 2: WAITS key scores [Hkv, T] fp32 from the pass-1 normalisers.
+    ``pass2`` picks the plan of long sequences: "auto" or "key_blocks"."""
     _last_dim_contiguous(q, k)
-    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     if out is None:
         out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
-    nbytes = colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale)
+    nbytes = colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale, pass2)
     ws = _workspace(nbytes, q.device, workspace)
     _check("waits_colsum", lib().waits_colsum(
         m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), _ptr(ws),
@@ -270,13 +278,13 @@ def colsum(q: torch.Tensor, k: torch.Tensor, lse_rows: torch.Tensor, cu_seqlens,
 
 def score(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
           out: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Both passes: WAITS key scores [Hkv, T] fp32."""
+          workspace: Optional[torch.Tensor] = None, pass2: str = "auto") -> torch.Tensor:
+    """Both passes: WAITS key scores [Hkv, T] fp32 (``pass2`` as in colsum)."""
     _last_dim_contiguous(q, k)
-    m = _Marshal(cu_seqlens, q, k, scale, a, b)
+    m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     if out is None:
         out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
-    nbytes = score_workspace_bytes(q, k, cu_seqlens, a, b, scale)
+    nbytes = score_workspace_bytes(q, k, cu_seqlens, a, b, scale, pass2)
     ws = _workspace(nbytes, q.device, workspace)
     _check("waits_score", lib().waits_score(
         m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), _ptr(ws),
@@ -383,9 +391,9 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, sca
     return out, lse
 
 
-def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None):
+def score_select_compact(q, k, v, cu_seqlens, a, b, budget, scale=None, pass2: str = "auto"):
     """The whole path: scores, kept positions and the compacted K/V."""
-    s = score(q, k, cu_seqlens, a, b, scale)
+    s = score(q, k, cu_seqlens, a, b, scale, pass2=pass2)
     idx, kc, vc = select_compact(s, k, v, cu_seqlens, budget)
     return s, idx, kc, vc
 

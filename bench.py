@@ -328,6 +328,40 @@ def counters_from(prof_dir: str, workload_name: str, copy_bytes: int):
     print(json.dumps(rec, indent=1), flush=True)
 
 
+def step_buffers(wl, q, k, cu):
+    """Device buffers of one step of a workload: lse, pass workspace, scores,
+    kept positions, compacted K/V and the select workspace, allocated once."""
+    import torch
+    import attention_score_eviction_amd as W
+
+    a, b, budget = wl["a"], wl["b"], wl["budget"]
+    T, hq, hkv, d = int(cu[-1]), wl["hq"], wl["hkv"], wl["d"]
+    B, dev = len(wl["lengths"]), q.device
+    ws_bytes = max(W.waits.lse_workspace_bytes(q, k, cu, a, b),
+                   W.waits.colsum_workspace_bytes(q, k, cu, a, b))
+    kc = torch.empty((B, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    return {"lse": torch.empty((hq, T), dtype=torch.float32, device=dev),
+            "ws": torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
+            "scores": torch.empty((hkv, T), dtype=torch.float32, device=dev),
+            "idx": torch.empty((B, hkv, budget), dtype=torch.int32, device=dev),
+            "kc": kc, "vc": torch.empty_like(kc),
+            "sel_ws": torch.empty(max(W.waits.select_workspace_bytes(cu, hkv, budget), 256),
+                                  dtype=torch.uint8, device=dev)}
+
+
+def step_calls(wl, q, k, v, cu, bf):
+    """The three library calls of one step (pass 1, pass 2, select+compact)."""
+    import attention_score_eviction_amd as W
+
+    a, b, budget = wl["a"], wl["b"], wl["budget"]
+    return [
+        lambda: W.lse(q, k, cu, a, b, out=bf["lse"], workspace=bf["ws"]),
+        lambda: W.colsum(q, k, bf["lse"], cu, a, b, out=bf["scores"], workspace=bf["ws"]),
+        lambda: W.select_compact(bf["scores"], k, v, cu, budget, idx=bf["idx"], k_out=bf["kc"],
+                                 v_out=bf["vc"], workspace=bf["sel_ws"]),
+    ]
+
+
 def stage_runners(fns, graph: bool):
     """One callable per stage of a step: the library calls themselves, or,
     with ``graph``, the replay of a HIP graph (torch.cuda.CUDAGraph) captured
@@ -583,25 +617,10 @@ def main():
     T, hq, hkv, d = int(cu[-1]), wl["hq"], wl["hkv"], wl["d"]
     B = len(wl["lengths"])
 
-    lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
-    ws_bytes = max(W.waits.lse_workspace_bytes(q, k, cu, a, b),
-                   W.waits.colsum_workspace_bytes(q, k, cu, a, b))
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    scores = torch.empty((hkv, T), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, hkv, budget), dtype=torch.int32, device=dev)
-    kc = torch.empty((B, hkv, budget, d), dtype=torch.bfloat16, device=dev)
-    sel_ws = torch.empty(max(W.waits.select_workspace_bytes(cu, hkv, budget), 256),
-                         dtype=torch.uint8, device=dev)
-    vc = torch.empty_like(kc)
-
+    bufs = step_buffers(wl, q, k, cu)
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-
-    runs = stage_runners([
-        lambda: W.lse(q, k, cu, a, b, out=lse, workspace=ws),
-        lambda: W.colsum(q, k, lse, cu, a, b, out=scores, workspace=ws),
-        lambda: W.select_compact(scores, k, v, cu, budget, idx=idx, k_out=kc, v_out=vc, workspace=sel_ws),
-    ], args.graph)
+    runs = stage_runners(step_calls(wl, q, k, v, cu, bufs), args.graph)
 
     def step(e=None):
         for j, run in enumerate(runs):

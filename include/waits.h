@@ -60,6 +60,23 @@ enum {
 
 enum { WAITS_BF16 = 0, WAITS_F32 = 1 };
 
+/*
+ * Pass-2 plan for sequences with more than 512 packed query rows (G x
+ * processed rows) per KV head; shorter ones always keep every row of a KV
+ * head in one workgroup.
+ * WAITS_PASS2_AUTO: pass 2 reuses pass 1's row blocks (512 packed rows
+ *   each), every block writing its column sums to the workspace as
+ *   [row block][n_kv_heads][N] fp32 per sequence, added per key in block
+ *   order; sequences whose partials would pass 1 GiB (2 GiB over a launch of
+ *   up to 32 sequences) take the key-block plan instead.
+ * WAITS_PASS2_KEY_BLOCKS: every such sequence runs pass 2 on blocks of 512
+ *   keys, each streaming the rows that can see it; a block's rows may be
+ *   cut into chunks whose partial sums take [chunk][n_kv_heads][T] fp32 of
+ *   workspace, added in chunk order.  Same definition, different summation
+ *   order (agreement to fp32 rounding, not bit for bit).
+ */
+enum { WAITS_PASS2_AUTO = 0, WAITS_PASS2_KEY_BLOCKS = 1 };
+
 typedef struct waits_shape {
   int32_t batch;              /* number of sequences, >= 1                     */
   const int64_t* cu_seqlens;  /* HOST array [batch + 1], cu[0] = 0, ascending */
@@ -70,6 +87,9 @@ typedef struct waits_shape {
   int64_t q_stride_tok, q_stride_head;   /* element strides of Q          */
   int64_t kv_stride_tok, kv_stride_head; /* element strides of K and V    */
   float scale;                /* softmax scale, finite > 0 (1/sqrt(head_dim)) */
+  int32_t pass2;              /* WAITS_PASS2_AUTO (0) or WAITS_PASS2_KEY_BLOCKS;
+                                 checked by every call that takes Q (any other
+                                 value: WAITS_EINVAL)                          */
 } waits_shape;
 
 /*

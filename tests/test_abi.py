@@ -160,12 +160,12 @@ def test_workspace_sizes():
     # with (max, sum) partials; pass 2 writes its scores directly
     assert W.lse_workspace_bytes(q, k, [0, 4096], [1.0], [16]) > 0
     assert W.colsum_workspace_bytes(q, k, [0, 4096], [1.0], [16]) == 0
-    # all rows live, one short sequence: too few row blocks / key blocks for
-    # the chip, so pass 1 splits keys and pass 2 splits rows (partial sums
-    # [chunk][Hkv][T] fp32)
+    # all rows live, one short sequence: too few row blocks for the chip, so
+    # pass 1 splits keys and pass 2 writes one partial column sum per row
+    # block ([row block][Hkv][N] fp32)
     lse_ws = W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1])
     col_ws = W.colsum_workspace_bytes(q, k, [0, 4096], [0.0], [1])
-    assert lse_ws > 0 and col_ws > 0 and col_ws % (8 * 4096 * 4) == 0
+    assert lse_ws > 0 and col_ws == 32 * 8 * 4096 * 4
     assert (W.score_workspace_bytes(q, k, [0, 4096], [0.0], [1])
             >= 32 * 4096 * 4 + max(lse_ws, col_ws))
 
@@ -198,6 +198,57 @@ def test_colsum_workspace_validation():
     assert colsum(None, 0) == W.WAITS_EWORKSPACE
     assert colsum(FAKE, need.value - 1) == W.WAITS_EWORKSPACE
     assert colsum(ctypes.c_void_p(0x100002), need.value) == W.WAITS_EWORKSPACE  # misaligned
+
+
+def test_pass2_plan_validation_and_workspace():
+    # the plan field is checked by every call that takes Q
+    s = _shape(n=4096, hq=32, hkv=8)
+    a, b = _ab(a=0.0, b=1)
+    s.pass2 = 2
+    assert _score(s, a, b) == W.WAITS_EINVAL
+    need = ctypes.c_size_t(0)
+    assert W.lib().waits_colsum_workspace_bytes(ctypes.byref(s), a.ctypes.data_as(W._FP),
+                                                b.ctypes.data_as(W._IP),
+                                                ctypes.byref(need)) == W.WAITS_EINVAL
+    # all rows live at N = 4096: the automatic plan reuses pass 1's 512-row
+    # blocks ([row block][Hkv][N] partials); the key-block plan cuts each
+    # 512-key block's rows into chunks ([chunk][Hkv][T] partials)
+    q = torch.empty((4096, 32, 64), dtype=torch.bfloat16)
+    k = torch.empty((4096, 8, 64), dtype=torch.bfloat16)
+    auto = W.colsum_workspace_bytes(q, k, [0, 4096], [0.0], [1])
+    kb = W.colsum_workspace_bytes(q, k, [0, 4096], [0.0], [1], pass2="key_blocks")
+    assert auto == (4 * 4096 // 512) * 8 * 4096 * 4
+    assert kb > 0 and kb % (8 * 4096 * 4) == 0
+    # pass 1 does not depend on the pass-2 plan
+    assert (W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1])
+            == W.lse_workspace_bytes(q, k, [0, 4096], [0.0], [1], pass2="key_blocks"))
+    # few rows per KV head: one workgroup holds them all, no partials either way
+    assert W.colsum_workspace_bytes(q, k, [0, 4096], [1.0], [16], pass2="key_blocks") == 0
+    with pytest.raises(ValueError):
+        W.colsum_workspace_bytes(q, k, [0, 4096], [0.0], [1], pass2="rows")
+
+
+def test_head_major_group_span_only_limits_key_blocks():
+    # head-major Q of a 2^20-token prompt: one token's rows of a 4-head group
+    # span 3 T d + d elements (> 2^29 bytes), which only the key-block kernel
+    # addresses from one buffer base.  About 200 processed rows per query
+    # head (800 packed rows per KV head) run pass 2 on row blocks in the
+    # automatic plan, so the call gets as far as the workspace check; the
+    # key-block plan refuses the layout.  No call here reaches a launch.
+    n, hq, d = 1 << 20, 4, 128
+    s = _shape(n=n, hq=hq, hkv=1, d=d)
+    s.q_stride_tok, s.q_stride_head = d, n * d
+    s.kv_stride_tok, s.kv_stride_head = d, n * d
+    a, b = _ab(a=89.0 / 200, b=1)
+    q0 = int(W.first_rows([0, n], a, b)[0])
+    assert 512 < hq * (n - q0) <= 1024
+
+    def colsum(plan):
+        s.pass2 = plan
+        return W.lib().waits_colsum(ctypes.byref(s), FAKE, FAKE, FAKE, a.ctypes.data_as(W._FP),
+                                    b.ctypes.data_as(W._IP), FAKE, None, 0, None)
+    assert colsum(W.WAITS_PASS2_AUTO) == W.WAITS_EWORKSPACE
+    assert colsum(W.WAITS_PASS2_KEY_BLOCKS) == W.WAITS_EUNSUPPORTED
 
 
 def test_binding_raises_without_library(monkeypatch):

@@ -6,8 +6,10 @@ Between replays the program runs its own eager work (another eager pass
 into separate buffers) and synchronises.  Before each replay the graph's
 output buffers are poisoned, so a replay that skipped a kernel shows up.
 The batches cover every launch shape of a step: few-rows passes with their
-lse combine, row-block pass 1 with key-block pass 2, and the one-launch and
-the seven-launch (more than 32768 keys) select+compact.
+lse combine, row-block pass 1 with pass 2 on the same row blocks and their
+block-order reduce (the automatic plan) or on key blocks with the row-chunk
+reduce (the key-block plan), and the select+compact of short heads (one
+launch) and of heads of more than 32768 keys (several launches).
 """
 from __future__ import annotations
 
@@ -66,18 +68,20 @@ def _replay_and_check(g, graph_bufs, eager_bufs, poison, eager_again):
             assert torch.equal(t, eager_bufs[name]), f"replay {rep}: {name} differs from the eager result"
 
 
-def test_graph_replays_match_eager_scores_select_compact():
+@pytest.mark.parametrize("plan", ["auto", "key_blocks"])
+def test_graph_replays_match_eager_scores_select_compact(plan):
     lengths = [3000, 40000, 700, 1, 5000]
     a = [1.0, math.inf, 0.0, 1.0, 0.01]
     b = [16, 16, 1, 1, 128]
     hq, hkv, d, budget = 8, 2, 128, 256
-    _say(f"graph: score + select + compact, lengths {lengths}")
+    _say(f"graph: score + select + compact, pass-2 plan {plan}, lengths {lengths}")
     bt = make_batch([61 + i for i in range(len(lengths))], lengths, hq, hkv, d, heavy=True)
     q, k, v = to_device(bt)
     cu = bt.cu_seqlens
     T, nb = int(cu[-1]), len(lengths)
     ws = torch.empty(max(W.waits.lse_workspace_bytes(q, k, cu, a, b),
-                         W.waits.colsum_workspace_bytes(q, k, cu, a, b), 256), dtype=torch.uint8, device=DEV)
+                         W.waits.colsum_workspace_bytes(q, k, cu, a, b, pass2=plan), 256),
+                     dtype=torch.uint8, device=DEV)
     sel_ws = torch.empty(max(W.waits.select_workspace_bytes(cu, hkv, budget), 256), dtype=torch.uint8,
                          device=DEV)
 
@@ -90,7 +94,7 @@ def test_graph_replays_match_eager_scores_select_compact():
 
     def run(bf):
         W.lse(q, k, cu, a, b, out=bf["lse"], workspace=ws)
-        W.colsum(q, k, bf["lse"], cu, a, b, out=bf["scores"], workspace=ws)
+        W.colsum(q, k, bf["lse"], cu, a, b, out=bf["scores"], workspace=ws, pass2=plan)
         W.select_compact(bf["scores"], k, v, cu, budget, idx=bf["idx"], k_out=bf["k_out"], v_out=bf["v_out"],
                          workspace=sel_ws)
 

@@ -1,9 +1,10 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
 Sizes: the oracle runs the full definition where it finishes in seconds
-(several tiles plus ragged tails); at the workloads' full sizes it checks
-sampled outputs it can compute exactly (tail keys, or rows above a weight
-floor with a stated bound) plus properties that hold at any size.
+(several tiles plus ragged tails).  At the workloads' full sizes it runs in
+full where the processed rows are few (rows above a weight floor with a
+stated bound), and elsewhere on whole KV heads, computed in worker processes
+(tests/oracle_pool.py), plus properties that hold at any size.
 """
 import math
 import sys
@@ -16,6 +17,7 @@ import attention_score_eviction_amd as W
 from oracle import waits_oracle as orc
 from synth import ACTIONS, make_batch, make_prompt
 
+import oracle_pool
 from parity import (DEV, check_compact, check_scores, check_select_exact,
                     check_select_vs_oracle, host_bits, to_device)
 
@@ -93,6 +95,40 @@ def test_llama31_8b_layers_batched():
     _full_check(bt, [1.0] * 3, [16] * 3, 128)
 
 
+@pytest.mark.timeout(600)
+def test_headline_batch_as_benchmarked():
+    # bench.py's default step, with its buffers and calls: 32 layers x
+    # N=16384 in one batch (a = 1, b = 16, budget 128).  Every KV head has 420
+    # packed rows, and the batch gives one workgroup per head, so both passes
+    # run whole key ranges in the 16-row-tile kernel: pass 1 writes lse
+    # directly (no key split, no combine, no pass-1 workspace).  The first
+    # and the last layer against the oracle in full; selection on every layer.
+    import bench
+    _say("headline batch as benchmarked: 32 x 16384")
+    wl = bench.workload("8b")
+    q, k, v, cu = bench.make_inputs(wl, DEV)
+    assert W.lse_workspace_bytes(q, k, cu, wl["a"], wl["b"]) == 0
+    bufs = bench.step_buffers(wl, q, k, cu)
+    for call in bench.step_calls(wl, q, k, v, cu, bufs):
+        call()
+    torch.cuda.synchronize()
+    s_gpu = bufs["scores"].cpu().numpy()
+    idx = bufs["idx"].cpu().numpy()
+    check_select_exact(idx, s_gpu, cu, wl["budget"])
+    scale = float(np.float32(1 / math.sqrt(128)))
+    for layer in (0, 31):
+        bt = make_prompt(wl["seeds"][layer], 16384, 32, 8, 128, heavy=True, dtype="bf16")
+        lo, hi = int(cu[layer]), int(cu[layer + 1])
+        # rows with w <= 1e-30 are left out of the oracle: |error| <= G*N*1e-30
+        s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, 32, 8, [1.0], [16], scale,
+                                 weight_floor=1e-30)
+        err = check_scores(s_gpu[:, lo:hi], s_ref)
+        check_select_vs_oracle(idx[layer:layer + 1], s_ref, bt.cu_seqlens, wl["budget"])
+        check_compact(bufs["kc"][layer:layer + 1], bufs["vc"][layer:layer + 1], bt.k_bits, bt.v_bits,
+                      idx[layer:layer + 1], bt.cu_seqlens)
+        _say(f"  layer {layer}: every key within {err:.2e}")
+
+
 @pytest.fixture(scope="module")
 def long_prompt():
     return make_prompt(2, 131072, 32, 8, 128, heavy=True, dtype="bf16")
@@ -111,14 +147,32 @@ def test_long_context_full_size(long_prompt, a, b):
     _full_check(long_prompt, [a], [b], 2048, weight_floor=1e-30)
 
 
-def test_long_context_h2o_sampled(long_prompt):
-    # a=0 at N=131072: every row is live; the oracle checks the last 48 keys
-    # exactly (they only see the last 48 rows) and the mass invariant holds
-    # for every key
-    _say("long N=131072 a=0 sampled")
+def _check_full_heads(s_gpu, idx, bt, p, heads, a, b, budget, pool, weight_floor=0.0):
+    """Every key of the given KV heads of prompt p against the oracle (the
+    per-key bar), and those heads' kept sets (the index-set rule)."""
+    lo, hi = int(bt.cu_seqlens[p]), int(bt.cu_seqlens[p + 1])
+    g = bt.n_q_heads // bt.n_kv_heads
+    scale = float(np.float32(1 / math.sqrt(bt.head_dim)))
+    for h in heads:
+        ref = oracle_pool.kv_head_scores(bt.q[lo:hi], bt.k[lo:hi], h, g, a, b, scale,
+                                         weight_floor=weight_floor, pool=pool)
+        err = check_scores(s_gpu[h, lo:hi], ref)
+        check_select_vs_oracle(idx[p:p + 1, h:h + 1], ref[None], [0, hi - lo], budget)
+        _say(f"  prompt {p} head {h}: every key within {err:.2e}")
+
+
+@pytest.mark.timeout(1200)
+def test_long_context_h2o_full_heads(long_prompt):
+    # a=0 at N=131072 (the H2O limit): every row is live and pass 2 runs on
+    # key blocks (row-block partials would take 4.3 GB).  Two whole KV heads
+    # against the oracle, key by key, with their kept sets; on every head the
+    # last 48 keys (they see only the last 48 rows) and the mass invariant
+    _say("long N=131072 a=0, two full KV heads")
     n = 131072
     bt = long_prompt
     s_gpu, idx, kc, vc = _run_all(bt, [0.0], [1], 2048)
+    with oracle_pool.make_pool() as pool:
+        _check_full_heads(s_gpu, idx, bt, 0, [0, 5], 0.0, 1, 2048, pool)
     tail = n - 48
     s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, 32, 8, [0.0], [1],
                              float(np.float32(1 / math.sqrt(128))), row_min=[tail])
@@ -129,6 +183,7 @@ def test_long_context_h2o_sampled(long_prompt):
     check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, bt.cu_seqlens)
 
 
+@pytest.mark.timeout(900)
 def test_row_block_and_key_block_pass2_in_one_launch():
     # a=0 everywhere: the 70000-token prompt's row-block partials (547 blocks x
     # 8 heads x 70000 keys, 1.2 GB) exceed the per-sequence cap, so its pass 2
@@ -139,17 +194,68 @@ def test_row_block_and_key_block_pass2_in_one_launch():
     bt = make_batch([91, 92], lens, 32, 8, 128, heavy=True)
     s_gpu, idx, kc, vc = _run_all(bt, [0.0, 0.0], [1, 1], 256)
     cu = bt.cu_seqlens
-    tail = lens[0] - 48
+    # the long prompt: two whole KV heads key by key, with their kept sets,
+    # and the mass invariant sum_k s[h, k] = G * N / 2 on every head
+    with oracle_pool.make_pool() as pool:
+        _check_full_heads(s_gpu, idx, bt, 0, [0, 3], 0.0, 1, 256, pool)
+    np.testing.assert_allclose(s_gpu[:, :lens[0]].astype(np.float64).sum(axis=1), 2.0 * lens[0],
+                               rtol=1e-4)
+    # the short prompt: every key of every head
     s_ref = orc.waits_scores(bt.q, bt.k, cu, 32, 8, [0.0, 0.0], [1, 1],
-                             float(np.float32(1 / math.sqrt(128))), row_min=[tail, 0])
-    # the long prompt: exact on its last 48 keys (they see only the last 48
-    # rows) and the mass invariant sum_k s[h, k] = G * N / 2 on every head
-    check_scores(s_gpu[:, tail:lens[0]], s_ref[:, tail:lens[0]])
-    np.testing.assert_allclose(s_gpu[:, :lens[0]].astype(np.float64).sum(axis=1), 2.0 * lens[0], rtol=1e-4)
-    # the short prompt: every key
+                             float(np.float32(1 / math.sqrt(128))), row_min=[lens[0], 0])
     check_scores(s_gpu[:, lens[0]:], s_ref[:, lens[0]:])
+    check_select_vs_oracle(idx[1:], s_ref[:, lens[0]:], [0, lens[1]], 256)
     check_select_exact(idx, s_gpu, cu, 256)
     check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, cu)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(12, 4, 128, "bf16"), (6, 2, 64, "bf16"),
+                                             (3, 1, 128, "bf16"), (14, 2, 64, "bf16"),
+                                             (7, 1, 128, "bf16"), (8, 2, 64, "f32")])
+def test_key_block_plan_full_definition(hq, hkv, d, dtype):
+    # pass 2 forced onto key blocks (the plan the longest a = 0 prompts take)
+    # at sizes the oracle finishes: G in {3, 4, 7}, head_dim 64 and 128, bf16
+    # and fp32; every row live (a = 0, a = 0.01) or about 1800 of 3000 (a =
+    # 0.05), so each KV head has 4K..21K packed rows cut into row chunks,
+    # whose partial sums colsum_reduce_kernel adds in chunk order
+    _say(f"key-block plan hq={hq} hkv={hkv} d={d} {dtype}")
+    bt = make_batch([41 + hq, 42 + hq], [3000, 1500], hq, hkv, d, heavy=True, dtype=dtype)
+    q, k, _ = to_device(bt)
+    cu = bt.cu_seqlens
+    for a, b in [(0.0, 1), (0.01, 128), (0.05, 16)]:
+        assert W.colsum_workspace_bytes(q, k, cu, [a, a], [b, b], pass2="key_blocks") > 0
+        scale = float(np.float32(1 / math.sqrt(d)))
+        s = W.score(q, k, cu, [a, a], [b, b], pass2="key_blocks").cpu().numpy()
+        s_ref = orc.waits_scores(bt.q, bt.k, cu, hq, hkv, [a, a], [b, b], scale)
+        check_scores(s, s_ref)
+        # the automatic plan (row blocks here) computes the same sums in
+        # another order: equal to fp32 rounding
+        s_auto = W.score(q, k, cu, [a, a], [b, b]).cpu().numpy()
+        np.testing.assert_allclose(s, s_auto, rtol=2e-5, atol=0)
+        idx = W.select(torch.from_numpy(s).to(DEV), cu, 128).cpu().numpy()
+        check_select_exact(idx, s, cu, 128)
+        check_select_vs_oracle(idx, s_ref, cu, 128)
+
+
+def test_key_block_plan_one_row_chunk_per_block():
+    # enough key blocks over the batch (8 KV heads x 256 blocks) that every
+    # block's rows form one chunk: the kernel writes the scores directly and
+    # the plan needs no workspace.  G = 1; about 590 processed rows per head
+    # (a = 0.15), so the oracle runs every key of every head.
+    n, h, d = 131072, 8, 64
+    _say(f"key-block plan, one row chunk per block, N={n}")
+    bt = make_prompt(57, n, h, h, d, heavy=True, dtype="bf16")
+    q, k, _ = to_device(bt)
+    cu = bt.cu_seqlens
+    a, b = [0.15], [1]
+    assert 512 < n - int(W.waits.first_rows(cu, a, b)[0]) <= 1024
+    assert W.colsum_workspace_bytes(q, k, cu, a, b, pass2="key_blocks") == 0
+    s = W.score(q, k, cu, a, b, pass2="key_blocks").cpu().numpy()
+    s_ref = orc.waits_scores(bt.q, bt.k, cu, h, h, a, b, float(np.float32(1 / math.sqrt(d))))
+    check_scores(s, s_ref)
+    idx = W.select(torch.from_numpy(s).to(DEV), cu, 2048).cpu().numpy()
+    check_select_exact(idx, s, cu, 2048)
+    check_select_vs_oracle(idx, s_ref, cu, 2048)
 
 
 @pytest.fixture(scope="module")
@@ -185,12 +291,18 @@ def test_mistral_ragged_batch_reduced():
     _full_check(bt, a, b, 256)
 
 
+@pytest.mark.timeout(900)
 def test_mistral_ragged_batch_full_size():
-    # lengths in [8192, 32768]; tail keys exact, selection and gather exact
+    # lengths in [8192, 32768], one launch; two whole KV heads of every
+    # prompt key by key with their kept sets, the tail keys of every head,
+    # the mass invariant, and the selection and gather exactly
     _say("mistral ragged full size")
     bt, a, b = _mistral_batch(8192, 32768)
     s_gpu, idx, kc, vc = _run_all(bt, a, b, 256)
     cu = bt.cu_seqlens
+    with oracle_pool.make_pool() as pool:
+        for p in range(8):
+            _check_full_heads(s_gpu, idx, bt, p, [p % 8, (p + 4) % 8], a[p], b[p], 256, pool)
     tails = [int(n) - 32 for n in bt.lengths]
     s_ref = orc.waits_scores(bt.q, bt.k, cu, 32, 8, a, b,
                              float(np.float32(1 / math.sqrt(128))), row_min=tails)
@@ -231,9 +343,9 @@ def test_softmax_scale_other_than_default(scale, dtype):
 @pytest.mark.parametrize("hq,hkv,d", [(3, 1, 64), (6, 2, 128), (10, 2, 64), (14, 2, 128)])
 def test_group_sizes_not_powers_of_two(hq, hkv, d):
     # G = 3, 3, 5, 7: packed rows interleave the G query heads of a position,
-    # so row tiles, row blocks and key-block row stages start mid-position;
-    # a = 1 runs the few-rows shapes, a = 0 row blocks and key blocks, a = inf
-    # with b = 40 the few-rows shapes at 120..280 packed rows
+    # so row tiles and row blocks start mid-position; a = 1 runs the few-rows
+    # shapes, a = 0 row blocks for both passes (key blocks: the key-block
+    # plan test), a = inf with b = 40 the few-rows shapes at 120..280 packed rows
     _say(f"group sizes hq={hq} hkv={hkv} d={d}")
     bt = make_batch([81 + hq, 82 + hq], [3000, 1500], hq, hkv, d, heavy=True)
     for a, b in [(1.0, 16), (0.0, 1), (math.inf, 40)]:
@@ -303,17 +415,19 @@ def test_uniform_attention_closed_form_on_gpu():
     np.testing.assert_allclose(s, g / 2 * (harm[n] - harm[:n]), rtol=2e-5)
 
 
-@pytest.mark.parametrize("a,b", [(1.0, 16), (0.0, 1)])
-def test_head_major_strides_match_token_major(a, b):
-    # a=1: one workgroup holds all rows; a=0: row blocks and key blocks
-    _say(f"head-major strides a={a}")
+@pytest.mark.parametrize("a,b,plan", [(1.0, 16, "auto"), (0.0, 1, "auto"), (0.0, 1, "key_blocks")])
+def test_head_major_strides_match_token_major(a, b, plan):
+    # a=1: one workgroup holds all rows; a=0: pass 2 on row blocks (the
+    # automatic plan) or on key blocks, whose row stages address the G heads
+    # of a group from one base
+    _say(f"head-major strides a={a} plan {plan}")
     bt = make_prompt(21, 999, 8, 2, 128, heavy=True)
     q, k, v = to_device(bt)
     qh = q.permute(1, 0, 2).contiguous().permute(1, 0, 2)   # [T, H, d] view of [H, T, d]
     kh = k.permute(1, 0, 2).contiguous().permute(1, 0, 2)
     assert qh.stride(0) == 128 and kh.stride(1) == 999 * 128
-    s1 = W.score(q, k, bt.cu_seqlens, [a], [b])
-    s2 = W.score(qh, kh, bt.cu_seqlens, [a], [b])
+    s1 = W.score(q, k, bt.cu_seqlens, [a], [b], pass2=plan)
+    s2 = W.score(qh, kh, bt.cu_seqlens, [a], [b], pass2=plan)
     assert torch.equal(s1, s2)
 
 

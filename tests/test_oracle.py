@@ -305,3 +305,21 @@ def test_sampling_restrictions_keep_their_stated_bounds():
     cut = orc.waits_scores(q, k, cu, hq, hkv, [0.3], [9], F32(0.25), weight_floor=floor)
     assert np.all(np.abs(cut - full) <= 2 * n * floor)
     assert np.any(cut != full)
+
+
+@pytest.mark.parametrize("a,b,floor", [(0.0, 1, 0.0), (0.05, 7, 0.0), (1.0, 16, 1e-30),
+                                       (math.inf, 40, 0.0)])
+def test_pooled_kv_head_scores_equal_the_oracle(a, b, floor):
+    # the full-size GPU checks add per-(query head, row range) oracle pieces
+    # computed in worker processes; on a small prompt that sum must equal
+    # waits_scores of the whole KV head to rounding
+    import oracle_pool
+    n, hq, hkv, d = 700, 6, 2, 64
+    bt = make_prompt(77, n, hq, hkv, d, heavy=True, dtype="bf16")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, hq, hkv, [a], [b], scale, weight_floor=floor)
+    with oracle_pool.make_pool() as pool:
+        for h in range(hkv):
+            got = oracle_pool.kv_head_scores(bt.q, bt.k, h, hq // hkv, a, b, scale,
+                                             weight_floor=floor, pool=pool)
+            np.testing.assert_allclose(got, ref[h], rtol=1e-12, atol=0)
