@@ -107,7 +107,7 @@ def test_headline_batch_as_benchmarked():
     _say("headline batch as benchmarked: 32 x 16384")
     wl = bench.workload("8b")
     q, k, v, cu = bench.make_inputs(wl, DEV)
-    assert W.lse_workspace_bytes(q, k, cu, wl["a"], wl["b"]) == 0
+    assert W.waits.lse_workspace_bytes(q, k, cu, wl["a"], wl["b"]) == 0
     bufs = bench.step_buffers(wl, q, k, cu)
     for call in bench.step_calls(wl, q, k, v, cu, bufs):
         call()
@@ -223,7 +223,7 @@ def test_key_block_plan_full_definition(hq, hkv, d, dtype):
     q, k, _ = to_device(bt)
     cu = bt.cu_seqlens
     for a, b in [(0.0, 1), (0.01, 128), (0.05, 16)]:
-        assert W.colsum_workspace_bytes(q, k, cu, [a, a], [b, b], pass2="key_blocks") > 0
+        assert W.waits.colsum_workspace_bytes(q, k, cu, [a, a], [b, b], pass2="key_blocks") > 0
         scale = float(np.float32(1 / math.sqrt(d)))
         s = W.score(q, k, cu, [a, a], [b, b], pass2="key_blocks").cpu().numpy()
         s_ref = orc.waits_scores(bt.q, bt.k, cu, hq, hkv, [a, a], [b, b], scale)
@@ -249,7 +249,7 @@ def test_key_block_plan_one_row_chunk_per_block():
     cu = bt.cu_seqlens
     a, b = [0.15], [1]
     assert 512 < n - int(W.waits.first_rows(cu, a, b)[0]) <= 1024
-    assert W.colsum_workspace_bytes(q, k, cu, a, b, pass2="key_blocks") == 0
+    assert W.waits.colsum_workspace_bytes(q, k, cu, a, b, pass2="key_blocks") == 0
     s = W.score(q, k, cu, a, b, pass2="key_blocks").cpu().numpy()
     s_ref = orc.waits_scores(bt.q, bt.k, cu, h, h, a, b, float(np.float32(1 / math.sqrt(d))))
     check_scores(s, s_ref)
