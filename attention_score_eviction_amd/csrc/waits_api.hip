@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "waits.h"
@@ -19,6 +20,14 @@
 #include "select_compact.hpp"
 #include "select_wide.hpp"
 #include "attention.hpp"
+
+// Scratch of waits_select_compact_noalloc (the wide select's digit
+// histograms and per-chunk counts), one copy per GPU for the life of the
+// process.  In host code `scratch` is a host-side stand-in, not a device
+// address: kernels get the address hipGetSymbolAddress reports for their
+// device (device_scratch below).
+constexpr size_t STATIC_SCRATCH_BYTES = WAITS_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
 
 namespace waits {
 namespace {
@@ -661,6 +670,22 @@ int check_gather(const waits_shape* s, const void* k, const void* v, const int32
   return WAITS_OK;
 }
 
+int run_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
+                int32_t budget, void* k_out, void* v_out, hipStream_t stream);
+
+int seq_len(const waits_shape* s, int i) { return (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]); }
+
+// Table of sequences [lo, hi) for the select and compact kernels, which read
+// only the lengths and token offsets.
+void fill_len_table(SeqTable& t, const waits_shape* s, int lo, int hi) {
+  std::memset(&t, 0, sizeof(t));
+  t.nb = hi - lo;
+  for (int i = lo; i < hi; ++i) {
+    t.n[i - lo] = seq_len(s, i);
+    t.tok0[i - lo] = s->cu_seqlens[i];
+  }
+}
+
 // Workspace of the several-workgroup select for sequences [lo, hi): the
 // per-(sequence, head) digit histograms, then one (above, equal) count pair
 // per chunk.  0 when every sequence is short enough for one workgroup.
@@ -668,32 +693,33 @@ struct WideWs {
   size_t hist_bytes = 0, count_bytes = 0;
   int items = 0;
 };
-WideWs wide_ws(const waits_shape* s, const std::vector<Seq>& v, int lo, int hi) {
+WideWs wide_ws(const waits_shape* s, int lo, int hi) {
   WideWs w;
   int gmax = 0;
-  for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+  for (int i = lo; i < hi; ++i) gmax = std::max(gmax, seq_len(s, i));
   if (gmax <= SEL_WIDE_MIN) return w;
-  for (int i = lo; i < hi; ++i) w.items += s->n_kv_heads * wide_chunks(v[i].n);
+  for (int i = lo; i < hi; ++i) w.items += s->n_kv_heads * wide_chunks(seq_len(s, i));
   w.hist_bytes = (size_t)(hi - lo) * s->n_kv_heads * 4 * 256 * sizeof(int);
   w.count_bytes = (size_t)w.items * sizeof(int2);
   return w;
 }
 
-size_t select_ws_bytes(const waits_shape* s, const std::vector<Seq>& v) {
+size_t select_ws_bytes(const waits_shape* s) {
   size_t mx = 0;
   for (int lo = 0; lo < s->batch; lo += MAXB) {
-    const WideWs w = wide_ws(s, v, lo, std::min(s->batch, lo + MAXB));
+    const WideWs w = wide_ws(s, lo, std::min(s->batch, lo + MAXB));
     mx = std::max(mx, w.hist_bytes + w.count_bytes);
   }
   return mx;
 }
 
+// Select (and, with FUSE, the gather) per launch group of up to MAXB
+// sequences.  Plans from cu_seqlens alone: no host allocation.
 template <bool FUSE>
 int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_t* idx,
                const void* k, const void* vv, void* k_out, void* v_out, void* ws, size_t ws_bytes,
                hipStream_t stream) {
-  const std::vector<Seq> v = plan_seqs(s, nullptr, nullptr);
-  const size_t need = select_ws_bytes(s, v);
+  const size_t need = select_ws_bytes(s);
   if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 16)))) return WAITS_EWORKSPACE;
   const int e = FUSE ? elt_bytes(s->dtype) : 0;
   const int row_bytes = FUSE ? s->head_dim * e : 0;
@@ -701,9 +727,9 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     const int hi = std::min(s->batch, lo + MAXB);
     const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
     int gmax = 0;
-    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, v[i].n);
+    for (int i = lo; i < hi; ++i) gmax = std::max(gmax, seq_len(s, i));
     if (gmax > SEL_WIDE_MIN) {
-      const WideWs w = wide_ws(s, v, lo, hi);
+      const WideWs w = wide_ws(s, lo, hi);
       WideArgs args;
       std::memset(&args, 0, sizeof(args));
       args.scores = scores;
@@ -720,11 +746,11 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
       args.st = strides_of(s);
       args.elt = e;
       args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
-      fill_table(args.tab, v, lo, hi, s->n_kv_heads);
+      fill_len_table(args.tab, s, lo, hi);
       int items = 0;
       for (int i = lo; i < hi; ++i) {
         args.tab.first[i - lo] = items;
-        items += s->n_kv_heads * wide_chunks(v[i].n);
+        items += s->n_kv_heads * wide_chunks(seq_len(s, i));
       }
       args.tab.first[hi - lo] = items;
       const int64_t words = (int64_t)(w.hist_bytes / sizeof(int));
@@ -757,7 +783,7 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     args.st = strides_of(s);
     args.elt = e;
     args.row_shift = FUSE ? __builtin_ctz(row_bytes / 16) : 0;
-    fill_table(args.tab, v, lo, hi, s->n_kv_heads);
+    fill_len_table(args.tab, s, lo, hi);
     const dim3 grid((hi - lo) * s->n_kv_heads);
     static_assert(SEL_WIDE_MIN == SEL_THREADS * 32, "one workgroup holds at most 32 keys per lane");
     if (gmax <= SEL_THREADS * 16)
@@ -767,6 +793,59 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     if (launched() != WAITS_OK) return WAITS_EDEVICE;
   }
   return WAITS_OK;
+}
+
+// The static scratch's address on the device `stream` belongs to (the
+// current device for the null stream), looked up on the first call for that
+// device, with the device current, and kept.
+constexpr int SCRATCH_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_DEVICES];
+void* scratch_ptr[SCRATCH_DEVICES];
+hipError_t scratch_rc[SCRATCH_DEVICES];
+
+int device_scratch(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return WAITS_EDEVICE;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return WAITS_EDEVICE;
+    dev = sd;
+  }
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return WAITS_EUNSUPPORTED;
+  std::call_once(scratch_once[dev], [dev, cur] {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) {
+      scratch_rc[dev] = hipErrorInvalidDevice;
+      return;
+    }
+    void* ptr = nullptr;
+    scratch_rc[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = ptr;
+    if (dev != cur) (void)hipSetDevice(cur);
+  });
+  if (scratch_rc[dev] != hipSuccess || !scratch_ptr[dev]) return WAITS_EDEVICE;
+  *out = scratch_ptr[dev];
+  return WAITS_OK;
+}
+
+int check_select_compact(const waits_shape* s, const float* scores, const void* k, const void* v,
+                         int32_t budget, int32_t* idx, void* k_out, void* v_out) {
+  int rc = check_shape(s, false);
+  if (rc == WAITS_OK) rc = check_select(s, scores, budget, idx);
+  if (rc == WAITS_OK) rc = check_gather(s, k, v, idx, budget, k_out, v_out);
+  return rc;
+}
+
+int run_select_compact(const waits_shape* s, const float* scores, const void* k, const void* v,
+                       int32_t budget, int32_t* idx, void* k_out, void* v_out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  if (budget > SEL_FUSE_MAX) {
+    const int rc = run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, ws,
+                                     ws_bytes, stream);
+    if (rc != WAITS_OK) return rc;
+    return run_compact(s, k, v, idx, budget, k_out, v_out, stream);
+  }
+  return run_select<true>(s, scores, budget, idx, k, v, k_out, v_out, ws, ws_bytes, stream);
 }
 
 // Prefill attention forward: one item per (sequence, KV head, block of
@@ -822,7 +901,6 @@ int run_attention(const waits_shape* s, const void* q, const void* k, const void
 
 int run_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
                 int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
-  const std::vector<Seq> sq = plan_seqs(s, nullptr, nullptr);
   const int e = elt_bytes(s->dtype);
   const int row_bytes = s->head_dim * e;
   const int rows_per_block = 256 / (row_bytes / 16);
@@ -840,7 +918,7 @@ int run_compact(const waits_shape* s, const void* k, const void* v, const int32_
     args.hkv = s->n_kv_heads;
     args.budget = budget;
     args.elt = e;
-    fill_table(args.tab, sq, lo, hi, s->n_kv_heads);
+    fill_len_table(args.tab, s, lo, hi);
     const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
     if (launched() != WAITS_OK) return WAITS_EDEVICE;
@@ -947,7 +1025,7 @@ int waits_select_workspace_bytes(const waits_shape* s, int32_t budget, size_t* b
   const int rc = check_select_shape(s, budget);
   if (rc != WAITS_OK) return rc;
   if (!bytes) return WAITS_EINVAL;
-  *bytes = select_ws_bytes(s, plan_seqs(s, nullptr, nullptr));
+  *bytes = select_ws_bytes(s);
   return WAITS_OK;
 }
 
@@ -970,17 +1048,24 @@ int waits_compact(const waits_shape* s, const void* k, const void* v, const int3
 int waits_select_compact(const waits_shape* s, const float* scores, const void* k, const void* v,
                          int32_t budget, int32_t* idx, void* k_out, void* v_out, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
-  int rc = check_shape(s, false);
-  if (rc == WAITS_OK) rc = check_select(s, scores, budget, idx);
-  if (rc == WAITS_OK) rc = check_gather(s, k, v, idx, budget, k_out, v_out);
+  const int rc = check_select_compact(s, scores, k, v, budget, idx, k_out, v_out);
   if (rc != WAITS_OK) return rc;
-  if (budget > SEL_FUSE_MAX) {
-    rc = run_select<false>(s, scores, budget, idx, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes,
-                           stream);
+  return run_select_compact(s, scores, k, v, budget, idx, k_out, v_out, ws, ws_bytes, stream);
+}
+
+int waits_select_compact_noalloc(const waits_shape* s, const float* scores, const void* k,
+                                 const void* v, int32_t budget, int32_t* idx, void* k_out,
+                                 void* v_out, hipStream_t stream) {
+  int rc = check_select_compact(s, scores, k, v, budget, idx, k_out, v_out);
+  if (rc != WAITS_OK) return rc;
+  const size_t need = select_ws_bytes(s);
+  if (need > STATIC_SCRATCH_BYTES) return WAITS_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = device_scratch(stream, &ws);
     if (rc != WAITS_OK) return rc;
-    return run_compact(s, k, v, idx, budget, k_out, v_out, stream);
   }
-  return run_select<true>(s, scores, budget, idx, k, v, k_out, v_out, ws, ws_bytes, stream);
+  return run_select_compact(s, scores, k, v, budget, idx, k_out, v_out, ws, need, stream);
 }
 
 const char* waits_strerror(int code) {
@@ -990,6 +1075,8 @@ const char* waits_strerror(int code) {
     case WAITS_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128)";
     case WAITS_EWORKSPACE: return "workspace missing or too small";
     case WAITS_EDEVICE: return "HIP runtime refused a kernel launch";
+    case WAITS_ESCRATCH:
+      return "batch needs more scratch than the no-allocation call's static 4 MiB (use the workspace call)";
     default: return "unknown WAITS status";
   }
 }

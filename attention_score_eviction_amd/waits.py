@@ -28,7 +28,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwaits.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "waits.h")
 
-WAITS_OK, WAITS_EINVAL, WAITS_EUNSUPPORTED, WAITS_EWORKSPACE, WAITS_EDEVICE = range(5)
+WAITS_OK, WAITS_EINVAL, WAITS_EUNSUPPORTED, WAITS_EWORKSPACE, WAITS_EDEVICE, WAITS_ESCRATCH = range(6)
+STATIC_SCRATCH_BYTES = 4 << 20   # WAITS_STATIC_SCRATCH_BYTES
 WAITS_BF16, WAITS_F32 = 0, 1
 WAITS_PASS2_AUTO, WAITS_PASS2_KEY_BLOCKS = 0, 1
 _PASS2 = {"auto": WAITS_PASS2_AUTO, "key_blocks": WAITS_PASS2_KEY_BLOCKS}
@@ -87,6 +88,7 @@ _SIGS = {
     "waits_select_workspace_bytes": [_SP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "waits_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P],
     "waits_select_compact": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "waits_select_compact_noalloc": [_SP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P],
     "waits_attention": [_SP, _P, _P, _P, _P, _P, _P],
     "waits_decode_workspace_bytes": [_DSP, ctypes.POINTER(ctypes.c_size_t)],
     "waits_decode": [_DSP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -365,6 +367,23 @@ def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_se
     _check("waits_select_compact", lib().waits_select_compact(
         m.sp, _ptr(scores), _ptr(k), _ptr(v), int(budget), _ptr(idx), _ptr(k_out), _ptr(v_out),
         _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+        _stream(k)))
+    return idx, k_out, v_out
+
+
+def select_compact_noalloc(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
+                           budget: int, idx: torch.Tensor, k_out: torch.Tensor, v_out: torch.Tensor):
+    """select_compact() with no workspace: the library's static per-GPU
+    scratch serves the select of long heads (calls on one GPU must not
+    overlap).  The outputs are the caller's; nothing is allocated."""
+    _last_dim_contiguous(k, v)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    m = _Marshal(cu_seqlens, None, k, 1.0)
+    if scores.shape[0] != k.shape[1]:
+        raise ValueError("scores must be [n_kv_heads, T]")
+    _check("waits_select_compact_noalloc", lib().waits_select_compact_noalloc(
+        m.sp, _ptr(scores), _ptr(k), _ptr(v), int(budget), _ptr(idx), _ptr(k_out), _ptr(v_out),
         _stream(k)))
     return idx, k_out, v_out
 

@@ -55,7 +55,9 @@ enum {
   WAITS_EINVAL = 1,       /* malformed argument (null, negative, NaN, ...) */
   WAITS_EUNSUPPORTED = 2, /* well-formed but not built (head_dim, dtype)   */
   WAITS_EWORKSPACE = 3,   /* workspace missing or smaller than required    */
-  WAITS_EDEVICE = 4       /* the HIP runtime refused a launch              */
+  WAITS_EDEVICE = 4,      /* the HIP runtime refused a launch              */
+  WAITS_ESCRATCH = 5      /* the no-allocation call's static scratch is too
+                             small for this batch                          */
 };
 
 enum { WAITS_BF16 = 0, WAITS_F32 = 1 };
@@ -229,6 +231,32 @@ int waits_select_compact(const waits_shape* shape, const float* scores,
                          const void* k, const void* v, int32_t select_budget,
                          int32_t* idx, void* k_out, void* v_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * waits_select_compact for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and the same outputs, layouts and
+ * error codes as waits_select_compact, bit for bit.  The select of heads of
+ * more than 32768 keys needs scratch (digit histograms and per-chunk counts:
+ * the bytes waits_select_workspace_bytes reports); this call takes it from a
+ * static device array of WAITS_STATIC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends, and returns WAITS_ESCRATCH
+ * for a batch that needs more: a launch group (32 sequences) with such a
+ * head needs 4 KiB per (sequence, KV head) plus 8 bytes per 4096 keys of
+ * each head, e.g. 1.1 MiB for 32 sequences x 8 KV heads of 131072 keys.
+ * - The scratch of a GPU is the copy on the device `stream` belongs to (the
+ *   current device for the null stream); the first call for a device looks
+ *   its address up (hipGetSymbolAddress) and keeps it.
+ * - Every call on a GPU shares that GPU's array and leaves its contents
+ *   behind; each call clears what it needs before use.  Calls that overlap
+ *   on one GPU (several streams or host threads at once) race on the array
+ *   and give undefined results: serialise them.
+ * - No device or host memory is allocated by this call.
+ */
+#define WAITS_STATIC_SCRATCH_BYTES (4u << 20)
+int waits_select_compact_noalloc(const waits_shape* shape, const float* scores,
+                                 const void* k, const void* v, int32_t select_budget,
+                                 int32_t* idx, void* k_out, void* v_out, hipStream_t stream);
 
 /*
  * Decode attention over the compacted cache

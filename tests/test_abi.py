@@ -338,3 +338,19 @@ def test_decode_binding_checks_layouts():
         W.decode(q.float(), kc, kc, lens)                         # mixed dtypes
     with pytest.raises(ValueError):
         W.decode(q[:, :, :32].contiguous(), kc, kc, lens)         # head_dim mismatch
+
+
+def test_noalloc_select_compact_rejects_batches_beyond_its_scratch():
+    # 32 sequences x 32 KV heads of 40000 keys: 4 MiB of digit histograms plus
+    # the per-chunk counts pass the static scratch; refused before any launch
+    lib = W.lib()
+    assert "scratch" in W.strerror(W.WAITS_ESCRATCH)
+    s = _shape(cu=[40000 * i for i in range(33)], hkv=32, hq=32)
+    need = ctypes.c_size_t(0)
+    assert lib.waits_select_workspace_bytes(ctypes.byref(s), 256, ctypes.byref(need)) == 0
+    assert need.value > W.STATIC_SCRATCH_BYTES
+    assert lib.waits_select_compact_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, 256, FAKE, FAKE, FAKE,
+                                            None) == W.WAITS_ESCRATCH
+    # argument checks come first, as in waits_select_compact
+    assert lib.waits_select_compact_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE,
+                                            None) == W.WAITS_EINVAL
