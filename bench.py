@@ -18,7 +18,11 @@ inside its calls).  On ROCm 7.2 a replay costs about 1 us more per kernel node
 than direct launches, so the default is direct calls.
 
     python bench.py [--steps K] [--warmup W] [--graph]
-                    [--workload 8b|1b|long|long_snap|long_tova|mistral|decode|fused]
+                    [--workload 8b|1b|long|long_snap|long_tova|long_a<A>_b<B>|mistral|decode|fused]
+
+``long_a<A>_b<B>`` is one point of the long-context sweep (N = 131072, A in
+{0, 1, inf}, B in {1, 16, 128}; ``long_a0`` stands for every B); ``long``,
+``long_snap`` and ``long_tova`` are a=1 b=16, a=inf b=16 and a=inf b=1.
 
 ``--workload decode`` measures the step after the path instead: one decoding
 step's attention over the compacted cache (64 sequences of the Llama-3.1-8B
@@ -56,6 +60,14 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
+# The long-context sweep a in {0, 1, inf} x b in {1, 16, 128} at N = 131072:
+# at a = 0 every weight is 1/2 whatever b is, so one run stands for all three.
+LONG_SWEEP = {f"long_a{'inf' if a == math.inf else int(a)}_b{b}": (a, b)
+              for a in (1.0, math.inf) for b in (1, 16, 128)}
+LONG_SWEEP["long_a0"] = (0.0, 1)
+WORKLOADS = ["8b", "1b", "long", "long_snap", "long_tova", *sorted(LONG_SWEEP), "mistral", "decode", "fused"]
+
+
 def workload(name: str):
     """(description, heads, d, lengths, seeds, a, b, budget)."""
     if name == "8b":
@@ -67,15 +79,14 @@ def workload(name: str):
         return dict(desc="Llama-3.2-1B layer shape, N=4096, five actions as five sequences, budget 128",
                     hq=32, hkv=8, d=64, lengths=[4096] * 5, seeds=[1] * 5,
                     a=[x[0] for x in ACTIONS], b=[x[1] for x in ACTIONS], budget=128, layers=5)
-    if name == "long":
-        return dict(desc="Llama-3.1-8B layer shape, one layer N=131072, a=1 b=16, budget 2048",
-                    hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[1.0], b=[16],
-                    budget=2048, layers=1)
-    if name in ("long_snap", "long_tova"):
-        b = 16 if name == "long_snap" else 1
-        return dict(desc=f"Llama-3.1-8B layer shape, one layer N=131072, a=inf b={b} "
-                         f"({'SnapKV' if b > 1 else 'TOVA'} limit), budget 2048",
-                    hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[math.inf], b=[b],
+    long_alias = {"long": "long_a1_b16", "long_snap": "long_ainf_b16", "long_tova": "long_ainf_b1"}
+    name = long_alias.get(name, name)
+    if name in LONG_SWEEP:
+        a, b = LONG_SWEEP[name]
+        limit = {0.0: " (H2O limit: w = 1/2 for every row, the same computation for every b)",
+                 math.inf: " (TOVA limit)" if b == 1 else " (SnapKV limit)"}.get(a, "")
+        return dict(desc=f"Llama-3.1-8B layer shape, one layer N=131072, a={a:g} b={b}{limit}, budget 2048",
+                    hq=32, hkv=8, d=128, lengths=[131072], seeds=[2], a=[a], b=[b],
                     budget=2048, layers=1)
     if name == "mistral":
         rng = np.random.default_rng(3)
@@ -161,34 +172,65 @@ def _host_info():
     return threads, blas, cpu
 
 
+def _oracle_work(n: int, a: float, b: int, hq: int) -> float:
+    """Score elements the oracle computes for one sequence (every live row
+    against every key it sees, for every query head)."""
+    return float(hq) * float(np.sum(live_rows_fp32(n, a, b) + 1))
+
+
 def cpu_baseline(wl, budget_s: float):
-    """The float64 oracle, as it stands, on a bounded sample of the workload:
-    whole sequences (all KV heads), taken in order until about ``budget_s``
-    seconds of CPU work have run (at least one), timed on this host's cores.
-    Reported in the GPU's unit: sequence tokens per second (one sequence =
-    one layer of one prompt)."""
+    """The float64 oracle, as it stands, on a bounded sample of the workload,
+    timed on this host's cores, in the GPU's unit (sequence tokens per second;
+    one sequence = one layer of one prompt).  Whole sequences (all KV heads,
+    with select+compact) are taken in order until about ``budget_s`` seconds
+    have run.  A sequence too large for the budget (e.g. every row live at
+    N = 131072) is sampled instead: the oracle runs on its last rows only
+    (``row_min``), sized to about ``budget_s``, and the rate is scaled by the
+    share of the sequence's score elements those rows hold."""
     from oracle import waits_oracle as orc
 
     scale = float(np.float32(1 / math.sqrt(wl["d"])))
-    done_tokens, spent, used = 0, 0.0, 0
+    hq, hkv, d = wl["hq"], wl["hkv"], wl["d"]
+    rate_guess = 1e8   # oracle score elements per second on 16 cores (measured order)
+    done_tokens, spent, used, sampled = 0.0, 0.0, 0, ""
     for i in range(len(wl["lengths"])):
-        n = wl["lengths"][i]
-        bt = make_prompt(wl["seeds"][i], n, wl["hq"], wl["hkv"], wl["d"], heavy=True, dtype="bf16")
-        t0 = time.perf_counter()
-        s = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, wl["hq"], wl["hkv"], wl["a"][i:i + 1],
-                             wl["b"][i:i + 1], scale)
-        idx = orc.waits_select(s, bt.cu_seqlens, wl["hkv"], wl["budget"])
-        orc.waits_compact(bt.k_bits, bt.v_bits, bt.cu_seqlens, idx)
-        spent += time.perf_counter() - t0
-        done_tokens += n
+        n, a, b = wl["lengths"][i], wl["a"][i], wl["b"][i]
+        work = _oracle_work(n, a, b, hq)
+        if used and (spent + work / rate_guess > 1.5 * budget_s):
+            break
+        bt = make_prompt(wl["seeds"][i], n, hq, hkv, d, heavy=True, dtype="bf16")
+        if work / rate_guess <= 1.5 * budget_s:
+            t0 = time.perf_counter()
+            s = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, hq, hkv, [a], [b], scale)
+            idx = orc.waits_select(s, bt.cu_seqlens, hkv, wl["budget"])
+            orc.waits_compact(bt.k_bits, bt.v_bits, bt.cu_seqlens, idx)
+            spent += time.perf_counter() - t0
+            done_tokens += n
+        else:
+            # the last rows, about budget_s of work (each sees about n keys)
+            rows = max(1, int(budget_s * rate_guess / (hq * n)))
+            row_min = n - rows
+            t0 = time.perf_counter()
+            s = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, hq, hkv, [a], [b], scale,
+                                 row_min=[row_min])
+            idx = orc.waits_select(s, bt.cu_seqlens, hkv, wl["budget"])
+            orc.waits_compact(bt.k_bits, bt.v_bits, bt.cu_seqlens, idx)
+            dt = time.perf_counter() - t0
+            w = orc.sigmoid_weights(n, a, b)
+            live = np.nonzero(w != 0.0)[0]
+            share = float(np.sum(live[live >= row_min] + 1)) / float(np.sum(live + 1))
+            spent += dt / share
+            done_tokens += n
+            sampled = (f"; sequence {i} sampled on its last {rows} rows ({share:.2e} of its score "
+                       f"elements, {dt:.1f} s), time scaled by 1/share")
         used += 1
         if spent >= budget_s:
             break
     threads, blas, cpu = _host_info()
     return {"value": done_tokens / spent, "unit": UNIT, "cores": threads, "kind": "oracle",
             "sample": f"first {used} of {len(wl['lengths'])} sequences of the workload "
-                      f"({done_tokens} tokens, all {wl['hkv']} KV heads), float64 numpy oracle "
-                      f"incl. select+compact, {spent:.1f} s; BLAS {blas}; "
+                      f"({int(done_tokens)} tokens, all {hkv} KV heads), float64 numpy oracle "
+                      f"incl. select+compact, {spent:.1f} s{sampled}; BLAS {blas}; "
                       f"{len(os.sched_getaffinity(0))} cpus in affinity; {cpu}"}
 
 
@@ -575,7 +617,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="8b",
-                    choices=["8b", "1b", "long", "long_snap", "long_tova", "mistral", "decode", "fused"])
+                    choices=WORKLOADS)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
