@@ -47,8 +47,11 @@ constexpr int KB_MIN_ROWS = 256;                  // key blocks: fewest rows per
 constexpr int KB_MAX_CHUNKS = 64;                 // key blocks: most row chunks
 constexpr int64_t SPAN_BYTES = int64_t(1) << 30;  // buffer-load span of one chunk (< 2^31)
 constexpr int SEL_WIDE_MIN = SEL_THREADS * 32;    // longer key ranges: select over several workgroups
-constexpr int64_t RB_PART_MAX = int64_t(1) << 30;        // BIG pass 2 in row blocks: one sequence's partials
-constexpr int64_t RB_PART_TOTAL = int64_t(2) << 30;      // ... and one launch group's
+// BIG pass 2 in row blocks while one launch group's partials take at most
+// this much workspace (6 GiB: a = 0 with 8 KV heads and G = 4 up to N ~ 160K;
+// it also keeps the reduce's per-group item count, sum of Hkv N, within int32)
+constexpr int64_t RB_PART_MAX = int64_t(6) << 30;        // one sequence's partials
+constexpr int64_t RB_PART_TOTAL = int64_t(6) << 30;      // ... and one launch group's
 
 // Few-rows workgroup shapes: a head takes the smallest that holds its packed
 // rows (row blocks of longer heads use the largest).  tiles: 32-row tiles per

@@ -69,7 +69,7 @@ enum { WAITS_BF16 = 0, WAITS_F32 = 1 };
  * WAITS_PASS2_AUTO: pass 2 reuses pass 1's row blocks (512 packed rows
  *   each), every block writing its column sums to the workspace as
  *   [row block][n_kv_heads][N] fp32 per sequence, added per key in block
- *   order; sequences whose partials would pass 1 GiB (2 GiB over a launch of
+ *   order; sequences whose partials would pass 6 GiB (6 GiB over a launch of
  *   up to 32 sequences) take the key-block plan instead.
  * WAITS_PASS2_KEY_BLOCKS: every such sequence runs pass 2 on blocks of 512
  *   keys, each streaming the rows that can see it; a block's rows may be

@@ -161,18 +161,43 @@ def _check_full_heads(s_gpu, idx, bt, p, heads, a, b, budget, pool, weight_floor
         _say(f"  prompt {p} head {h}: every key within {err:.2e}")
 
 
+H2O_HEADS = (0, 5)
+
+
+@pytest.fixture(scope="module")
+def long_h2o_ref(long_prompt):
+    """Oracle scores of two whole KV heads of the long prompt at a = 0."""
+    bt = long_prompt
+    scale = float(np.float32(1 / math.sqrt(128)))
+    with oracle_pool.make_pool() as pool:
+        return {h: oracle_pool.kv_head_scores(bt.q, bt.k, h, 4, 0.0, 1, scale, pool=pool)
+                for h in H2O_HEADS}
+
+
+def _check_h2o_heads(s_gpu, idx, ref, lo, n, budget, what):
+    for h, r in ref.items():
+        err = check_scores(s_gpu[h, lo:lo + n], r)
+        check_select_vs_oracle(idx[:, h:h + 1], r[None], [0, n], budget)
+        _say(f"  {what} head {h}: every key within {err:.2e}")
+
+
 @pytest.mark.timeout(1200)
-def test_long_context_h2o_full_heads(long_prompt):
-    # a=0 at N=131072 (the H2O limit): every row is live and pass 2 runs on
-    # key blocks (row-block partials would take 4.3 GB).  Two whole KV heads
-    # against the oracle, key by key, with their kept sets; on every head the
-    # last 48 keys (they see only the last 48 rows) and the mass invariant
-    _say("long N=131072 a=0, two full KV heads")
+@pytest.mark.parametrize("plan", ["auto", "key_blocks"])
+def test_long_context_h2o_full_heads(long_prompt, long_h2o_ref, plan):
+    # a=0 at N=131072 (the H2O limit): every row is live; pass 2 runs on row
+    # blocks (4 GiB of per-block partials) in the automatic plan, on key
+    # blocks in the key-block plan.  Two whole KV heads against the oracle,
+    # key by key, with their kept sets; on every head the last 48 keys (they
+    # see only the last 48 rows) and the mass invariant
+    _say(f"long N=131072 a=0, plan {plan}, two full KV heads")
     n = 131072
     bt = long_prompt
-    s_gpu, idx, kc, vc = _run_all(bt, [0.0], [1], 2048)
-    with oracle_pool.make_pool() as pool:
-        _check_full_heads(s_gpu, idx, bt, 0, [0, 5], 0.0, 1, 2048, pool)
+    q, k, v = to_device(bt)
+    s = W.score(q, k, bt.cu_seqlens, [0.0], [1], pass2=plan)
+    idx, kc, vc = W.select_compact(s, k, v, bt.cu_seqlens, 2048)
+    torch.cuda.synchronize()
+    s_gpu, idx = s.cpu().numpy(), idx.cpu().numpy()
+    _check_h2o_heads(s_gpu, idx, long_h2o_ref, 0, n, 2048, plan)
     tail = n - 48
     s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, 32, 8, [0.0], [1],
                              float(np.float32(1 / math.sqrt(128))), row_min=[tail])
@@ -184,29 +209,34 @@ def test_long_context_h2o_full_heads(long_prompt):
 
 
 @pytest.mark.timeout(900)
-def test_row_block_and_key_block_pass2_in_one_launch():
-    # a=0 everywhere: the 70000-token prompt's row-block partials (547 blocks x
-    # 8 heads x 70000 keys, 1.2 GB) exceed the per-sequence cap, so its pass 2
-    # runs on key blocks; the 1500-token prompt's runs on row blocks with a
-    # block-order reduce.  Both share one launch group and one workspace.
-    _say("pass 2 on key blocks and row blocks in one batch")
-    lens = [70000, 1500]
-    bt = make_batch([91, 92], lens, 32, 8, 128, heavy=True)
-    s_gpu, idx, kc, vc = _run_all(bt, [0.0, 0.0], [1, 1], 256)
-    cu = bt.cu_seqlens
-    # the long prompt: two whole KV heads key by key, with their kept sets,
-    # and the mass invariant sum_k s[h, k] = G * N / 2 on every head
-    with oracle_pool.make_pool() as pool:
-        _check_full_heads(s_gpu, idx, bt, 0, [0, 3], 0.0, 1, 256, pool)
-    np.testing.assert_allclose(s_gpu[:, :lens[0]].astype(np.float64).sum(axis=1), 2.0 * lens[0],
-                               rtol=1e-4)
-    # the short prompt: every key of every head
-    s_ref = orc.waits_scores(bt.q, bt.k, cu, 32, 8, [0.0, 0.0], [1, 1],
-                             float(np.float32(1 / math.sqrt(128))), row_min=[lens[0], 0])
-    check_scores(s_gpu[:, lens[0]:], s_ref[:, lens[0]:])
-    check_select_vs_oracle(idx[1:], s_ref[:, lens[0]:], [0, lens[1]], 256)
-    check_select_exact(idx, s_gpu, cu, 256)
-    check_compact(kc, vc, bt.k_bits, bt.v_bits, idx, cu)
+def test_row_block_and_key_block_pass2_in_one_launch(long_prompt, long_h2o_ref):
+    # the long prompt twice in one batch at a = 0: the first sequence's
+    # row-block partials (4 GiB) fit the automatic plan's 6 GiB per launch
+    # group, the second's would pass it, so the second runs pass 2 on key
+    # blocks in the same launch group and workspace.  Both copies against the
+    # oracle on two whole KV heads, and against each other on every key.
+    _say("pass 2 on row blocks and key blocks in one batch: the long prompt twice")
+    n = 131072
+    bt = long_prompt
+    q1, k1, v1 = to_device(bt)
+    q, k, v = (torch.cat([x, x]) for x in (q1, k1, v1))
+    del q1, k1, v1
+    cu = np.array([0, n, 2 * n], dtype=np.int64)
+    ws = W.waits.colsum_workspace_bytes(q, k, cu, [0.0, 0.0], [1, 1])
+    rb_one = 1024 * 8 * n * 4          # one copy's row-block partials: 1024 blocks x 8 heads x N
+    assert rb_one <= ws < 2 * rb_one   # the other copy's key-block chunks are far smaller
+    s = W.score(q, k, cu, [0.0, 0.0], [1, 1])
+    idx, kc, vc = W.select_compact(s, k, v, cu, 2048)
+    torch.cuda.synchronize()
+    s_gpu, idx = s.cpu().numpy(), idx.cpu().numpy()
+    for p in range(2):
+        _check_h2o_heads(s_gpu, idx[p:p + 1], long_h2o_ref, p * n, n, 2048, f"copy {p}")
+    # the same sums in two orders: equal to fp32 rounding
+    np.testing.assert_allclose(s_gpu[:, n:], s_gpu[:, :n], rtol=2e-5, atol=0)
+    check_select_exact(idx, s_gpu, cu, 2048)
+    kb = np.concatenate([bt.k_bits, bt.k_bits])
+    vb = np.concatenate([bt.v_bits, bt.v_bits])
+    check_compact(kc, vc, kb, vb, idx, cu)
 
 
 @pytest.mark.parametrize("hq,hkv,d,dtype", [(12, 4, 128, "bf16"), (6, 2, 64, "bf16"),
