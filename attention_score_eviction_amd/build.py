@@ -16,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libwaits.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# instruction-mix microbenchmarks (bench.py --ubench); not part of the path
+UBENCH_PATH = os.path.join(PKG, "libwaits_ubench.so")
 ARCH = "gfx950"
 
 
@@ -26,7 +28,7 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libwaits.so)")
 
 
-def compile_command(out: str) -> list:
+def compile_command(out: str, sources=("waits_api.hip", "decode_api.hip")) -> list:
     return [
         _hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # no packed fp32 VALU instructions in device code
@@ -37,13 +39,13 @@ def compile_command(out: str) -> list:
         "-mllvm", "-amdgpu-sched-strategy=max-ilp",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
-        os.path.join(CSRC, "waits_api.hip"), os.path.join(CSRC, "decode_api.hip"), "-o", out,
+        *[os.path.join(CSRC, src) for src in sources], "-o", out,
     ]
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
+def _compile(path: str, sources, verbose: bool) -> None:
+    tmp = path + ".tmp"
+    cmd = compile_command(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,7 +55,13 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Builds libwaits.so and the microbenchmark library; returns libwaits.so's path."""
+    _compile(LIB_PATH, ("waits_api.hip", "decode_api.hip"), verbose)
+    _compile(UBENCH_PATH, ("ubench.hip",), verbose)
     return LIB_PATH
 
 

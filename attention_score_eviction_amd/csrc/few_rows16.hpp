@@ -15,10 +15,11 @@
 // Work item, staging and stage loop follow few_rows_kernel: 8 waves, wave w
 // owns the 16-row tiles w + 8 t (t < NT); K moves HBM -> registers (a ring of
 // FR_RING stages of buffer loads) -> LDS (double buffer, one barrier per
-// 128-key stage) -> every wave; the MFMAs of 32-key sub-tile g share a basic
-// block with the epilogue of sub-tile g - 1, with no branch between them on
-// sub-tiles below every row's diagonal.  A wave holds NT or NT - 1 live
-// tiles: two copies of the stage loop, chosen once per wave.
+// 128-key stage) -> every wave; the MFMAs of 32-key sub-tile g issue as one
+// cluster at raised wave priority, followed in the same basic block by the
+// epilogue of sub-tile g - 1, with no branch between them on sub-tiles below
+// every row's diagonal.  A wave holds NT or NT - 1 live tiles: two copies of
+// the stage loop, chosen once per wave.
 //
 // Pass 1: MFMA(A = K tile, B = Q rows): a lane owns one query row and 8 keys
 // of a 32-key sub-tile; lazy exponent reference as in few_rows_kernel; the
@@ -366,20 +367,29 @@ few_rows16_kernel(const FrArgs args) {
   };
 
   // Sub-tile g of LDS stage buffer buf, slot u (parity par = u & 1, a
-  // constant): MFMAs into acc[par] in the same block as the epilogue of
-  // sub-tile g - 1 from acc[par ^ 1].
+  // constant): the MFMAs into acc[par] issue as one cluster at raised wave
+  // priority, then the epilogue of sub-tile g - 1 from acc[par ^ 1] at normal
+  // priority (s_setprio also keeps the compiler from interleaving the two:
+  // the matrix core and the exponential epilogue overlap only partly inside a
+  // wave, and this order measured 3-4% faster than the interleaved one).
+  // csum starts at -0, so the first add of a key's sum folds away (x + -0 is
+  // x for every x; the flush's sums start at +0).
   auto subtile = [&](int buf, int u, int g, auto par_c, auto ntv_c) __attribute__((always_inline)) {
     constexpr int par = decltype(par_c)::value;
     const int j = g - 1;
     const bool clean = j >= 0 && j < nsub && kbeg + j * TILE + TILE - 1 <= q0;
-    float csum[2] = {0.f, 0.f};
+    float csum[2] = {-0.f, -0.f};
     if (clean) {
       read_k(buf, u);
+      __builtin_amdgcn_s_setprio(1);
       mma(par, ntv_c);
+      __builtin_amdgcn_s_setprio(0);
       epi_clean(par ^ 1, ntv_c, csum);
     } else {
       read_k(buf, u);
+      __builtin_amdgcn_s_setprio(1);
       mma(par, ntv_c);
+      __builtin_amdgcn_s_setprio(0);
       epi_general(par ^ 1, j, ntv_c, csum);
     }
     if constexpr (PASS2) {

@@ -1,0 +1,169 @@
+// Microbenchmarks of the QK^T passes' instruction mix on gfx950: what one
+// 16x16x32 bf16 MFMA, one exponential epilogue element-instruction triple
+// (v_fma_f32, v_exp_f32, v_add_f32, as in p = exp2(s * c - off); sum += p)
+// and their combinations cost per SIMD.  Measurement only: built into its
+// own library (libwaits_ubench.so), never part of the WAITS path.
+//
+// Every wave runs ITERS iterations of one mode's loop body (8 independent
+// MFMA chains and/or 8 independent VALU chains, so issue rate and not
+// latency bounds it) and records its shader-clock cycles (s_memtime) and
+// 100 MHz real-time ticks (s_memrealtime).  Waves w and w + 4 of a workgroup
+// share a SIMD (hardware wave -> SIMD map, also reported), so 256 threads
+// put one wave on each SIMD of a CU, 512 threads two.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum Mode {
+  M_MFMA = 0,        // 8 MFMAs
+  M_TRIPLE = 1,      // 8 (fma, exp, add) triples
+  M_EXP = 2,         // 8 exps
+  M_FMA = 3,         // 8 fmas
+  M_ADD = 4,         // 8 adds
+  M_MIXED = 5,       // 8 MFMAs and 8 triples, interleaved by the compiler
+  M_CLUSTERS = 6,    // 8 MFMAs, then 8 triples (scheduling barrier between)
+  M_PRIO = 7,        // as M_CLUSTERS, MFMAs at raised wave priority
+  M_SPLIT_TRIPLE = 8,  // waves < W/2: 8 MFMAs; the others: 8 triples
+  M_SPLIT_FMA = 9,     // waves < W/2: 8 MFMAs; the others: 8 fmas
+  M_SPLIT_EXP = 10,    // waves < W/2: 8 MFMAs; the others: 8 exps
+  N_MODES = 11
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(512) mix_kernel(float* out, long long* stamps, int iters, float c) {
+  constexpr int NM = 8, NV = 8;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (tid + i));
+    b[i] = (__bf16)(0.002f * (tid - i));
+  }
+  f32x4 acc[NM];
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float x[NV], sum[NV];
+  for (int v = 0; v < NV; ++v) {
+    x[v] = 0.01f * (tid + v);
+    sum[v] = 0.f;
+  }
+  const bool split = MODE >= M_SPLIT_TRIPLE;
+  const bool do_m = MODE == M_MFMA || MODE == M_MIXED || MODE == M_CLUSTERS || MODE == M_PRIO ||
+                    (split && wave < nw / 2);
+  const bool do_v = (MODE >= M_TRIPLE && MODE <= M_PRIO) || (split && wave >= nw / 2);
+  constexpr bool triple = MODE == M_TRIPLE || MODE == M_MIXED || MODE == M_CLUSTERS || MODE == M_PRIO ||
+                          MODE == M_SPLIT_TRIPLE;
+  __syncthreads();
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    if (do_m) {
+      if constexpr (MODE == M_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[m], 0, 0, 0);
+      if constexpr (MODE == M_PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    if constexpr (MODE == M_CLUSTERS) __builtin_amdgcn_sched_barrier(0);
+    if (do_v) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        if constexpr (triple) {
+          sum[v] += __builtin_amdgcn_exp2f(fmaf(x[v], c, -sum[v]));
+        } else if constexpr (MODE == M_EXP || MODE == M_SPLIT_EXP) {
+          x[v] = __builtin_amdgcn_exp2f(x[v]);
+        } else if constexpr (MODE == M_FMA || MODE == M_SPLIT_FMA) {
+          x[v] = fmaf(x[v], c, -x[v]);
+        } else {
+          x[v] = x[v] + c;
+        }
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  float r = 0.f;
+  for (int m = 0; m < NM; ++m) r += acc[m][0] + acc[m][3];
+  for (int v = 0; v < NV; ++v) r += sum[v] + x[v];
+  out[blockIdx.x * blockDim.x + tid] = r;
+  if ((tid & 63) == 0) {
+    const int w = blockIdx.x * nw + wave;
+    stamps[2 * w] = t1 - t0;
+    stamps[2 * w + 1] = r1 - r0;
+  }
+}
+
+// HW_ID (hwreg 4): bits 5:4 = SIMD of the wave
+__global__ void simd_map_kernel(int* out) {
+  const unsigned hw = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+  if ((threadIdx.x & 63) == 0) out[threadIdx.x >> 6] = (int)((hw >> 4) & 3);
+}
+
+template <int MODE>
+int run_mode(int threads, int blocks, int iters, float* out, long long* stamps, double* res) {
+  hipLaunchKernelGGL(mix_kernel<MODE>, dim3(blocks), dim3(threads), 0, 0, out, stamps, 16, 1.0001f);
+  hipLaunchKernelGGL(mix_kernel<MODE>, dim3(blocks), dim3(threads), 0, 0, out, stamps, iters, 1.0001f);
+  if (hipDeviceSynchronize() != hipSuccess) return 4;
+  const int nw = threads / 64, waves = blocks * nw;
+  std::vector<long long> h((size_t)waves * 2);
+  if (hipMemcpy(h.data(), stamps, sizeof(long long) * h.size(), hipMemcpyDeviceToHost) != hipSuccess) return 4;
+  long long mx[2] = {0, 0}, rt = 0;
+  for (int w = 0; w < waves; ++w) {
+    const int half = (w % nw) >= nw / 2;
+    mx[half] = std::max(mx[half], h[2 * w]);
+    rt = std::max(rt, h[2 * w + 1]);
+  }
+  res[0] = (double)mx[0] / iters;   // cycles per iteration, slowest wave of the first half
+  res[1] = (double)mx[1] / iters;   // ... of the second half
+  res[2] = (double)std::max(mx[0], mx[1]) / ((double)rt / 100e6) / 1e9;   // shader clock, GHz
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Runs every mode on `blocks` workgroups of `threads` (256 or 512) threads
+// for `iters` iterations; res[3 * mode + {0, 1, 2}] = cycles per iteration
+// of the slowest wave of the first and of the second half of each
+// workgroup's waves, and the shader clock in GHz.  simd[w] (w < threads/64)
+// = the SIMD wave w of a workgroup ran on.  Returns 0, or 4 on a HIP error.
+int waits_ubench_mix(int threads, int blocks, int iters, double* res, int* simd) {
+  if (threads != 256 && threads != 512) return 1;
+  float* out = nullptr;
+  long long* stamps = nullptr;
+  int* map = nullptr;
+  if (hipMalloc(&out, sizeof(float) * blocks * threads) != hipSuccess) return 4;
+  if (hipMalloc(&stamps, sizeof(long long) * 2 * blocks * (threads / 64)) != hipSuccess) return 4;
+  if (hipMalloc(&map, sizeof(int) * 16) != hipSuccess) return 4;
+  int rc = 0;
+  rc = rc ? rc : run_mode<M_MFMA>(threads, blocks, iters, out, stamps, res + 3 * M_MFMA);
+  rc = rc ? rc : run_mode<M_TRIPLE>(threads, blocks, iters, out, stamps, res + 3 * M_TRIPLE);
+  rc = rc ? rc : run_mode<M_EXP>(threads, blocks, iters, out, stamps, res + 3 * M_EXP);
+  rc = rc ? rc : run_mode<M_FMA>(threads, blocks, iters, out, stamps, res + 3 * M_FMA);
+  rc = rc ? rc : run_mode<M_ADD>(threads, blocks, iters, out, stamps, res + 3 * M_ADD);
+  rc = rc ? rc : run_mode<M_MIXED>(threads, blocks, iters, out, stamps, res + 3 * M_MIXED);
+  rc = rc ? rc : run_mode<M_CLUSTERS>(threads, blocks, iters, out, stamps, res + 3 * M_CLUSTERS);
+  rc = rc ? rc : run_mode<M_PRIO>(threads, blocks, iters, out, stamps, res + 3 * M_PRIO);
+  rc = rc ? rc : run_mode<M_SPLIT_TRIPLE>(threads, blocks, iters, out, stamps, res + 3 * M_SPLIT_TRIPLE);
+  rc = rc ? rc : run_mode<M_SPLIT_FMA>(threads, blocks, iters, out, stamps, res + 3 * M_SPLIT_FMA);
+  rc = rc ? rc : run_mode<M_SPLIT_EXP>(threads, blocks, iters, out, stamps, res + 3 * M_SPLIT_EXP);
+  if (rc == 0) {
+    hipLaunchKernelGGL(simd_map_kernel, dim3(1), dim3(threads), 0, 0, map);
+    if (hipMemcpy(simd, map, sizeof(int) * (threads / 64), hipMemcpyDeviceToHost) != hipSuccess) rc = 4;
+  }
+  (void)hipFree(out);
+  (void)hipFree(stamps);
+  (void)hipFree(map);
+  return rc;
+}
+
+int waits_ubench_modes(void) { return N_MODES; }
+
+}  // extern "C"

@@ -609,6 +609,36 @@ def fused_bench(args):
     print(json.dumps(res), flush=True)
 
 
+UBENCH_MODES = ["mfma: 8 MFMA 16x16x32 bf16", "triple: 8 (fma, exp, add)", "exp: 8 v_exp_f32",
+                "fma: 8 v_fma_f32", "add: 8 v_add_f32", "mixed: 8 MFMA + 8 triples, compiler's interleave",
+                "clusters: 8 MFMA then 8 triples", "clusters, MFMA at raised wave priority",
+                "split: waves 0-3 8 MFMA, waves 4-7 8 triples",
+                "split: waves 0-3 8 MFMA, waves 4-7 8 fma", "split: waves 0-3 8 MFMA, waves 4-7 8 exp"]
+
+
+def ubench(args):
+    """Instruction-mix microbenchmarks of the QK^T passes (libwaits_ubench.so):
+    cycles per loop iteration of the slowest wave of each half of the
+    workgroup's waves, per mode, at one and two waves per SIMD."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "attention_score_eviction_amd", "libwaits_ubench.so"))
+    n = lib.waits_ubench_modes()
+    assert n == len(UBENCH_MODES)
+    for threads in (256, 512):
+        res = (ctypes.c_double * (3 * n))()
+        simd = (ctypes.c_int * 16)()
+        rc = lib.waits_ubench_mix(threads, 256, 4000, res, simd)
+        if rc:
+            raise SystemExit(f"waits_ubench_mix failed ({rc})")
+        print(json.dumps({"ubench": "instruction mix", "threads": threads, "workgroups": 256,
+                          "waves_per_simd": threads // 256,
+                          "simd_of_wave": list(simd[:threads // 64]),
+                          "cycles_per_iteration": {m: {"waves_first_half": round(res[3 * i], 1),
+                                                       "waves_second_half": round(res[3 * i + 1], 1),
+                                                       "clock_ghz": round(res[3 * i + 2], 3)}
+                                                   for i, m in enumerate(UBENCH_MODES)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,10 +654,15 @@ def main():
                     help="replay each stage from a captured HIP graph instead of calling the library")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--ubench", action="store_true",
+                    help="only run the instruction-mix microbenchmarks (libwaits_ubench.so) and exit")
     ap.add_argument("--counters-from", metavar="DIR",
                     help="only write profiles/traffic_<workload>.json from rocprofv3 runs in DIR "
                          "(fetch/, write/, cfetch/, cwrite/, trace/) and exit; no GPU needed")
     args = ap.parse_args()
+    if args.ubench:
+        ubench(args)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
