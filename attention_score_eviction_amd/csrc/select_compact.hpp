@@ -3,7 +3,8 @@
 // introduction's retained key-value pairs are then gathered).
 //
 // select_kernel: one 1024-thread workgroup per (sequence, KV head).  Scores
-// are non-negative fp32, so their bit patterns order like the values; an
+// are non-negative fp32, so their bit patterns order like the values (a
+// pattern with the sign bit set, -0 included, counts as +0); an
 // MSB-first radix select (4 digits of 8 bits) finds the bit pattern T of the
 // budget-th largest score and how many of the kept keys must equal T.  Keys
 // above T, then the lowest-positioned keys equal to T (ties go to the lower
@@ -53,6 +54,11 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int SEL_SUB = 32;          // sub-counters per digit
 constexpr int SEL_FUSE_MAX = 8192;   // largest budget the fused gather keeps in LDS
+
+// The order key of a score's bit pattern: non-negative floats order like
+// their bit patterns; anything with the sign bit set (-0, and values outside
+// the scores' domain) counts as +0.
+__device__ __forceinline__ uint32_t sel_key(uint32_t u) { return (int32_t)u < 0 ? 0u : u; }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -119,14 +125,15 @@ select_kernel(const SelectArgs args) {
       if constexpr (FUSE) sel[j] = j;
     }
   } else {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)h * args.T + tab.tok0[p]);
+    // Range-checked buffer loads: a slot at or past N reads 0 without a
+    // branch, so the PTC loads issue back to back.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(args.scores + (int64_t)h * args.T + tab.tok0[p]), 0, N * 4, BUFFER_RSRC_WORD3);
     const int e0 = wave * (PTC * WAVE) + lane;  // slot i of this lane: key e0 + 64 i
     uint32_t u[PTC];
 #pragma unroll
-    for (int i = 0; i < PTC; ++i) {
-      const int e = e0 + i * WAVE;
-      u[i] = e < N ? s[e] : 0u;
-    }
+    for (int i = 0; i < PTC; ++i)
+      u[i] = sel_key((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (e0 + i * WAVE) * 4, 0, 0));
     for (int i = tid; i < 256 * SEL_SUB / 4; i += SEL_THREADS)
       reinterpret_cast<int4*>(sub)[i] = int4{0, 0, 0, 0};
     hist[tid >> 8][tid & 255] = 0;

@@ -57,7 +57,7 @@ struct WideArgs {
 // Where a workgroup's chunk sits and what it loads.
 struct WideItem {
   int p, h, ch, nch, N, keep, c0;
-  const uint32_t* s;          // the head's scores
+  __amdgpu_buffer_rsrc_t rs;  // the head's scores (loads past N read 0)
   int* hist;                  // the head's 4 x 256 histogram
 };
 
@@ -73,19 +73,22 @@ __device__ __forceinline__ WideItem wide_item(const WideArgs& args) {
   w.ch = local - w.h * w.nch;
   w.keep = min(args.budget, w.N);
   w.c0 = w.ch * WIDE_CHUNK;
-  w.s = reinterpret_cast<const uint32_t*>(args.scores + (int64_t)w.h * args.T + tab.tok0[w.p]);
+  const float* sc = args.scores + (int64_t)w.h * args.T + tab.tok0[w.p];
+  w.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), 0, w.N * 4, BUFFER_RSRC_WORD3);
   w.hist = args.hist + ((int64_t)w.p * args.hkv + w.h) * 4 * 256;
   return w;
 }
 
 // This lane's keys of the chunk (wave w owns [c0 + w * WIDE_SEG, + WIDE_SEG),
-// lane l its keys c0 + w * WIDE_SEG + 64 i + l): validity and bit patterns.
+// lane l its keys c0 + w * WIDE_SEG + 64 i + l): validity and order keys.
+// Range-checked buffer loads (0 past N) keep the loads unconditional, so all
+// of a lane's loads are in flight together.
 __device__ __forceinline__ void wide_load(const WideItem& w, int wave, int lane, uint32_t* u, bool* ok) {
 #pragma unroll
   for (int i = 0; i < WIDE_PER; ++i) {
     const int e = w.c0 + wave * WIDE_SEG + i * WAVE + lane;
     ok[i] = e < w.N;
-    u[i] = ok[i] ? w.s[e] : 0u;
+    u[i] = sel_key((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(w.rs, e * 4, 0, 0));
   }
 }
 

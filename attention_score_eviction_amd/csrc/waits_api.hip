@@ -716,6 +716,30 @@ size_t select_ws_bytes(const waits_shape* s) {
   return mx;
 }
 
+// The gather of sequences [lo, hi) from their kept positions.
+int launch_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx, int32_t budget,
+                   void* k_out, void* v_out, int lo, int hi, hipStream_t stream) {
+  const int e = elt_bytes(s->dtype);
+  const int row_bytes = s->head_dim * e;
+  const int rows_per_block = 256 / (row_bytes / 16);
+  const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
+  CompactArgs args;
+  args.k = static_cast<const unsigned char*>(k);
+  args.v = static_cast<const unsigned char*>(v);
+  args.idx = idx + first_row;
+  args.k_out = static_cast<unsigned char*>(k_out) + first_row * row_bytes;
+  args.v_out = static_cast<unsigned char*>(v_out) + first_row * row_bytes;
+  args.st = strides_of(s);
+  args.rows = (int64_t)(hi - lo) * s->n_kv_heads * budget;
+  args.hkv = s->n_kv_heads;
+  args.budget = budget;
+  args.elt = e;
+  fill_len_table(args.tab, s, lo, hi);
+  const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
+  return launched();
+}
+
 // Select (and, with FUSE, the gather) per launch group of up to MAXB
 // sequences.  Plans from cu_seqlens alone: no host allocation.
 template <bool FUSE>
@@ -904,27 +928,9 @@ int run_attention(const waits_shape* s, const void* q, const void* k, const void
 
 int run_compact(const waits_shape* s, const void* k, const void* v, const int32_t* idx,
                 int32_t budget, void* k_out, void* v_out, hipStream_t stream) {
-  const int e = elt_bytes(s->dtype);
-  const int row_bytes = s->head_dim * e;
-  const int rows_per_block = 256 / (row_bytes / 16);
   for (int lo = 0; lo < s->batch; lo += MAXB) {
     const int hi = std::min(s->batch, lo + MAXB);
-    const int64_t first_row = (int64_t)lo * s->n_kv_heads * budget;
-    CompactArgs args;
-    args.k = static_cast<const unsigned char*>(k);
-    args.v = static_cast<const unsigned char*>(v);
-    args.idx = idx + first_row;
-    args.k_out = static_cast<unsigned char*>(k_out) + first_row * row_bytes;
-    args.v_out = static_cast<unsigned char*>(v_out) + first_row * row_bytes;
-    args.st = strides_of(s);
-    args.rows = (int64_t)(hi - lo) * s->n_kv_heads * budget;
-    args.hkv = s->n_kv_heads;
-    args.budget = budget;
-    args.elt = e;
-    fill_len_table(args.tab, s, lo, hi);
-    const int64_t blocks = (args.rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args, row_bytes);
-    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+    if (launch_compact(s, k, v, idx, budget, k_out, v_out, lo, hi, stream) != WAITS_OK) return WAITS_EDEVICE;
   }
   return WAITS_OK;
 }
