@@ -60,18 +60,34 @@ struct FrArgs {
   SeqTable tab;               // nc / kc: key chunks; first[]: items
 };
 
-// FR_WAVES waves, each owning FR_TW row tiles: ROWS = FR_WAVES * FR_TW * 32
-// packed rows per workgroup (a head with fewer rows takes the smallest
-// workgroup that holds them, so short windows do not pad to FR_ROWS).
+// LDS of a workgroup of FR_WAVES waves, each owning FR_TW row tiles: ROWS =
+// FR_WAVES * FR_TW * 32 packed rows (a head with fewer rows takes the
+// smallest workgroup that holds them, so short windows do not pad to
+// FR_ROWS).  Stages are SUB 32-key sub-tiles (one barrier each); smaller
+// workgroups take shorter stages to keep each thread's share of the load
+// ring small.
+template <typename T, int D, int FR_WAVES, int FR_TW>
+struct FrLds {
+  static constexpr int ROWS = FR_WAVES * FR_TW * TILE;
+  static constexpr int SUB = FR_WAVES >= 8 ? 4 : 2;
+  alignas(16) unsigned char lds[2][SUB][TileGeom<T, D>::LDS_BYTES];  // K double buffer
+  alignas(16) float row_off[ROWS];   // pass 2: exponent offsets
+  alignas(16) int row_q[ROWS];       // row position (-1: padding)
+  // pass 2: per-wave key sums of a sub-tile; 2 SUB slots, so one stage's
+  // stores never meet the previous stage's flushes; key k: [2k], [2k + 1]
+  alignas(16) float red[2 * SUB][FR_WAVES][2 * TILE];
+};
+
+// One work item on threads [0, FR_WAVES * 64) of the workgroup: `item` is
+// its index among the items of `first` (first work item of each sequence),
+// L the workgroup's LDS.
 template <typename T, int D, bool PASS2, int FR_WAVES, int FR_TW>
-__global__ void __launch_bounds__(FR_WAVES * WAVE)
-few_rows_kernel(const FrArgs args) {
+__device__ __forceinline__ void few_rows_body(const FrArgs& args, const int32_t* first, int item,
+                                              FrLds<T, D, FR_WAVES, FR_TW>& L) {
   constexpr int FR_THREADS = FR_WAVES * WAVE;
   constexpr int ROWS = FR_WAVES * FR_TW * TILE;
   static_assert(ROWS <= FR_ROWS, "at most FR_ROWS rows per workgroup");
-  // 32-key sub-tiles per stage (one barrier each); smaller workgroups take
-  // shorter stages to keep each thread's share of the load ring small
-  constexpr int FR_SUB = FR_WAVES >= 8 ? 4 : 2;
+  constexpr int FR_SUB = FrLds<T, D, FR_WAVES, FR_TW>::SUB;
   constexpr int FR_STAGE = FR_SUB * TILE;
   using Geo = TileGeom<T, D>;
   constexpr int HALF = Geo::ROW_BYTES / 2;
@@ -79,17 +95,14 @@ few_rows_kernel(const FrArgs args) {
   constexpr int CHUNKS = FR_STAGE * CPR;                       // per stage
   constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;   // chunks per thread per stage
   static_assert(FR_SUB % 2 == 0, "accumulator parity follows the sub-tile index");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float row_off[ROWS];   // pass 2: exponent offsets
-  __shared__ __attribute__((aligned(16))) int row_q[ROWS];       // row position (-1: padding)
-  // pass 2: per-wave key sums of a sub-tile; 2 FR_SUB slots, so one stage's
-  // stores never meet the previous stage's flushes
-  __shared__ __attribute__((aligned(16))) float red[2 * FR_SUB][FR_WAVES][2 * TILE];  // key k: [2k], [2k + 1]
+  auto& lds = L.lds;
+  auto& row_off = L.row_off;
+  auto& row_q = L.row_q;
+  auto& red = L.red;
 
   const SeqTable& tab = args.tab;
-  const int item = blockIdx.x;
-  const int p = find_seq(tab.first, tab.nb, item);
-  const int local = item - tab.first[p];
+  const int p = find_seq(first, tab.nb, item);
+  const int local = item - first[p];
   const int hkv = args.hkv, G = args.G;
   const int h = local % hkv;
   const int rest = local / hkv;
@@ -500,6 +513,13 @@ few_rows_kernel(const FrArgs args) {
       }
     }
   }
+}
+
+template <typename T, int D, bool PASS2, int FR_WAVES, int FR_TW>
+__global__ void __launch_bounds__(FR_WAVES * WAVE)
+few_rows_kernel(const FrArgs args) {
+  __shared__ FrLds<T, D, FR_WAVES, FR_TW> L;
+  few_rows_body<T, D, PASS2, FR_WAVES, FR_TW>(args, args.tab.first, blockIdx.x, L);
 }
 
 // Pass 2 of heads in several row blocks: a key's score is the sum, in

@@ -40,9 +40,21 @@ struct IntC {
   static constexpr int value = V;
 };
 
+// LDS of the 16-row-tile workgroup (8 waves, NT tiles each; 4 sub-tiles per stage).
+template <int D, int NT>
+struct Fr16Lds {
+  static constexpr int ROWS = 8 * NT * 16;
+  alignas(16) unsigned char lds[2][4][TileGeom<bf16_t, D>::LDS_BYTES];  // K double buffer
+  alignas(16) float row_off[ROWS];
+  alignas(16) int row_q[ROWS];
+  alignas(16) float red[2 * 4][8][2 * TILE];  // key k: [2k], [2k + 1]
+};
+
+// One work item (index `item` among the items of `first`) on the whole
+// 512-thread workgroup, L its LDS.
 template <int D, bool PASS2, int NT>
-__global__ void __launch_bounds__(512)
-few_rows16_kernel(const FrArgs args) {
+__device__ __forceinline__ void few_rows16_body(const FrArgs& args, const int32_t* first, int item,
+                                                Fr16Lds<D, NT>& L) {
   using T = bf16_t;
   using Geo = TileGeom<T, D>;
   constexpr int FR_WAVES = 8;
@@ -57,15 +69,14 @@ few_rows16_kernel(const FrArgs args) {
   constexpr int CHUNKS = FR_STAGE * CPR;
   constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;
   static_assert(FR_RING % 2 == 0, "LDS buffer parity follows the unrolled stage index");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][FR_SUB][Geo::LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float row_off[ROWS];
-  __shared__ __attribute__((aligned(16))) int row_q[ROWS];
-  __shared__ __attribute__((aligned(16))) float red[2 * FR_SUB][FR_WAVES][2 * TILE];  // key k: [2k], [2k + 1]
+  auto& lds = L.lds;
+  auto& row_off = L.row_off;
+  auto& row_q = L.row_q;
+  auto& red = L.red;
 
   const SeqTable& tab = args.tab;
-  const int item = blockIdx.x;
-  const int p = find_seq(tab.first, tab.nb, item);
-  const int local = item - tab.first[p];
+  const int p = find_seq(first, tab.nb, item);
+  const int local = item - first[p];
   const int hkv = args.hkv, G = args.G;
   const int h = local % hkv;
   const int chunk = local / hkv;  // one row block: the whole head
@@ -483,6 +494,13 @@ few_rows16_kernel(const FrArgs args) {
       }
     }
   }
+}
+
+template <int D, bool PASS2, int NT>
+__global__ void __launch_bounds__(512)
+few_rows16_kernel(const FrArgs args) {
+  __shared__ Fr16Lds<D, NT> L;
+  few_rows16_body<D, PASS2, NT>(args, args.tab.first, blockIdx.x, L);
 }
 
 }  // namespace waits

@@ -16,6 +16,7 @@
 #include "pass2_colsum.hpp"
 #include "few_rows.hpp"
 #include "few_rows16.hpp"
+#include "few_rows_multi.hpp"
 #include "key_blocks.hpp"
 #include "select_compact.hpp"
 #include "select_wide.hpp"
@@ -398,6 +399,45 @@ void dispatch_fr(const waits_shape* s, const FrArgs& args, int items, int shape,
   }
 }
 
+static_assert(FR_MULTI_SHAPES == FR_NSHAPES, "one launch segment per shape");
+static_assert(sizeof(FrMultiArgs) <= 4096, "kernel argument segment");
+
+// The few-rows launches of one pass: items[sh] work items on shape sh,
+// firsts[sh] the first item of each sequence among them.  Heads of several
+// shapes in a bf16 batch go into one few_rows_multi_kernel launch, the
+// row-block shape's segment first; otherwise each shape has its own launch.
+template <bool PASS2>
+int launch_fr_shapes(const waits_shape* s, const FrArgs& f, const int* items,
+                     const int32_t (*firsts)[MAXB + 1], hipStream_t st) {
+  int active = 0;
+  for (int sh = 0; sh < FR_NSHAPES; ++sh) active += items[sh] > 0 ? 1 : 0;
+  if (s->dtype == WAITS_BF16 && active > 1) {
+    FrMultiArgs m;
+    std::memset(&m, 0, sizeof(m));
+    m.f = f;
+    int at = 0;
+    for (int sh = FR_NSHAPES - 1; sh >= 0; --sh) {
+      m.begin[sh] = at;
+      at += items[sh];
+      m.end[sh] = at;
+      std::memcpy(m.first[sh], firsts[sh], sizeof(m.first[sh]));
+    }
+    if (s->head_dim == 64)
+      hipLaunchKernelGGL((few_rows_multi_kernel<64, PASS2>), dim3(at), dim3(8 * WAVE), 0, st, m);
+    else
+      hipLaunchKernelGGL((few_rows_multi_kernel<128, PASS2>), dim3(at), dim3(8 * WAVE), 0, st, m);
+    return launched();
+  }
+  for (int sh = 0; sh < FR_NSHAPES; ++sh) {
+    if (items[sh] == 0) continue;
+    FrArgs g = f;
+    std::memcpy(g.tab.first, firsts[sh], sizeof(g.tab.first));
+    dispatch_fr<PASS2>(s, g, items[sh], sh, st);
+    if (launched() != WAITS_OK) return WAITS_EDEVICE;
+  }
+  return WAITS_OK;
+}
+
 FrArgs fr_args(const waits_shape* s, const void* q, const void* k) {
   FrArgs f;
   std::memset(&f, 0, sizeof(f));
@@ -423,23 +463,23 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
     SeqTable tab;
     fill_table(tab, v, lo, hi, hkv);
 
-    // few-rows kernel: one launch per workgroup shape
-    for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+    // few-rows kernel: the heads of every workgroup shape
+    {
       FrArgs f = fr_args(s, q, k);
       f.lse = lse;
       f.part = static_cast<float2*>(ws);
       f.tab = tab;
-      int fr_items = 0;
-      for (int i = lo; i < hi; ++i) {
-        f.tab.first[i - lo] = fr_items;
-        if ((v[i].mode == Mode::FR || v[i].mode == Mode::BIG) && v[i].frs == shape)
-          fr_items += hkv * v[i].nrb * v[i].nc;
+      int items[FR_NSHAPES] = {};
+      int32_t firsts[FR_NSHAPES][MAXB + 1] = {};
+      for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+        for (int i = lo; i < hi; ++i) {
+          firsts[shape][i - lo] = items[shape];
+          if ((v[i].mode == Mode::FR || v[i].mode == Mode::BIG) && v[i].frs == shape)
+            items[shape] += hkv * v[i].nrb * v[i].nc;
+        }
+        firsts[shape][hi - lo] = items[shape];
       }
-      f.tab.first[hi - lo] = fr_items;
-      if (fr_items > 0) {
-        dispatch_fr<false>(s, f, fr_items, shape, stream);
-        if (launched() != WAITS_OK) return WAITS_EDEVICE;
-      }
+      if (launch_fr_shapes<false>(s, f, items, firsts, stream) != WAITS_OK) return WAITS_EDEVICE;
     }
 
     // fp32 rows of head_dim 128
@@ -529,25 +569,25 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
       if (v[i].mode == Mode::BIG && v[i].p2rb) rb_off += (int64_t)v[i].nrb * hkv * v[i].n;
     }
 
-    // few-rows sequences, and the row blocks of longer ones: one launch per workgroup shape
-    for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+    // few-rows sequences, and the row blocks of longer ones, on every workgroup shape
+    {
       FrArgs f = fr_args(s, q, k);
       f.lse = const_cast<float*>(lse);
       f.scores = scores;
       f.cpart = cpart;
       f.tab = rbtab;
-      int fr_items = 0;
-      for (int i = lo; i < hi; ++i) {
-        f.tab.first[i - lo] = fr_items;
-        if (v[i].frs != shape) continue;
-        if (v[i].mode == Mode::FR) fr_items += hkv * v[i].nc;
-        else if (v[i].mode == Mode::BIG && v[i].p2rb) fr_items += hkv * v[i].nrb * v[i].nc;
+      int items[FR_NSHAPES] = {};
+      int32_t firsts[FR_NSHAPES][MAXB + 1] = {};
+      for (int shape = 0; shape < FR_NSHAPES; ++shape) {
+        for (int i = lo; i < hi; ++i) {
+          firsts[shape][i - lo] = items[shape];
+          if (v[i].frs != shape) continue;
+          if (v[i].mode == Mode::FR) items[shape] += hkv * v[i].nc;
+          else if (v[i].mode == Mode::BIG && v[i].p2rb) items[shape] += hkv * v[i].nrb * v[i].nc;
+        }
+        firsts[shape][hi - lo] = items[shape];
       }
-      f.tab.first[hi - lo] = fr_items;
-      if (fr_items > 0) {
-        dispatch_fr<true>(s, f, fr_items, shape, stream);
-        if (launched() != WAITS_OK) return WAITS_EDEVICE;
-      }
+      if (launch_fr_shapes<true>(s, f, items, firsts, stream) != WAITS_OK) return WAITS_EDEVICE;
     }
     {
       RowBlockReduceArgs ra;

@@ -36,12 +36,13 @@ def _run_all(bt, a, b, budget, scale=None):
     return s.cpu().numpy(), idx.cpu().numpy(), kc, vc
 
 
-def _full_check(bt, a, b, budget, scale=None, weight_floor=0.0):
+def _full_check(bt, a, b, budget, scale=None, weight_floor=0.0, s_ref=None):
     d = bt.head_dim
     scale = np.float32(1 / math.sqrt(d)) if scale is None else np.float32(scale)
     s_gpu, idx, kc, vc = _run_all(bt, a, b, budget, float(scale))
-    s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, bt.n_q_heads, bt.n_kv_heads,
-                             a, b, float(scale), weight_floor=weight_floor)
+    if s_ref is None:
+        s_ref = orc.waits_scores(bt.q, bt.k, bt.cu_seqlens, bt.n_q_heads, bt.n_kv_heads,
+                                 a, b, float(scale), weight_floor=weight_floor)
     err = check_scores(s_gpu, s_ref)
     check_select_exact(idx, s_gpu, bt.cu_seqlens, budget)
     check_select_vs_oracle(idx, s_ref, bt.cu_seqlens, budget)
@@ -73,11 +74,60 @@ def llama1b():
     return make_prompt(1, 4096, 32, 8, 64, heavy=True, dtype="bf16")
 
 
+@pytest.fixture(scope="module")
+def llama1b_refs(llama1b):
+    """The oracle's scores of the 1B prompt, per action, computed once."""
+    scale = float(np.float32(1 / math.sqrt(64)))
+    refs = {}
+
+    def ref(a, b):
+        if (a, b) not in refs:
+            refs[(a, b)] = orc.waits_scores(llama1b.q, llama1b.k, llama1b.cu_seqlens, 32, 8, [a], [b], scale)
+        return refs[(a, b)]
+    return ref
+
+
 @pytest.mark.parametrize("a,b", list(ACTIONS))
-def test_llama32_1b_layer(llama1b, a, b):
+def test_llama32_1b_layer(llama1b, llama1b_refs, a, b):
     # 32 query heads, 8 KV heads, d=64, N=4096, heavy hitters, budget 128
     _say(f"llama3.2-1b a={a} b={b}")
-    _full_check(llama1b, [a], [b], 128)
+    _full_check(llama1b, [a], [b], 128, s_ref=llama1b_refs(a, b))
+
+
+@pytest.mark.timeout(300)
+def test_1b_batch_as_benchmarked(llama1b, llama1b_refs):
+    # bench.py's 1b step, with its buffers and calls: the five actions as five
+    # sequences of one batch, all on the 1B prompt.  The batch mixes the
+    # few-rows workgroup shapes (row blocks at a = 0 and a = 0.01, the 16-row
+    # kernel at a = 1, the 2- and 4-wave shapes at a = 10), whose launches run
+    # side by side on separate streams.  Every key of every sequence against
+    # the oracle; a second step gives the same bits.
+    import bench
+    _say("1b batch as benchmarked: five actions x 4096")
+    wl = bench.workload("1b")
+    assert [(a, b) for a, b in zip(wl["a"], wl["b"])] == list(ACTIONS)
+    q, k, v, cu = bench.make_inputs(wl, DEV)
+    bufs = bench.step_buffers(wl, q, k, cu)
+    calls = bench.step_calls(wl, q, k, v, cu, bufs)
+    outs = []
+    for _ in range(2):
+        for call in calls:
+            call()
+        torch.cuda.synchronize()
+        outs.append({n: bufs[n].cpu() for n in ("lse", "scores", "idx", "kc", "vc")})
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), f"{n} differs between two steps"
+    s_gpu = outs[0]["scores"].numpy()
+    idx = outs[0]["idx"].numpy()
+    check_select_exact(idx, s_gpu, cu, wl["budget"])
+    for p, (a, b) in enumerate(ACTIONS):
+        lo, hi = int(cu[p]), int(cu[p + 1])
+        s_ref = llama1b_refs(a, b)
+        err = check_scores(s_gpu[:, lo:hi], s_ref)
+        check_select_vs_oracle(idx[p:p + 1], s_ref, llama1b.cu_seqlens, wl["budget"])
+        check_compact(bufs["kc"][p:p + 1], bufs["vc"][p:p + 1], llama1b.k_bits, llama1b.v_bits,
+                      idx[p:p + 1], llama1b.cu_seqlens)
+        _say(f"  a={a} b={b}: every key within {err:.2e}")
 
 
 def test_llama31_8b_layer_full_size():
