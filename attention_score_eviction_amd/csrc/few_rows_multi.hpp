@@ -6,13 +6,11 @@
 // heads on several workgroup shapes.  One launch per shape makes each wait
 // for the previous one's tail, with most compute units idle; here the
 // shapes' work items share one grid of 512-thread workgroups.  Segment s of
-// the grid, [begin[s], end[s]), holds the items of shape s; the host lays
-// the row-block shape out first, so its long items start first and the
-// short ones fill the compute units its tail leaves.  A workgroup of a shape
-// with fewer than 8 waves ends its other waves at once; the hardware barrier
-// then waits only for the waves still running.  The LDS is the union of the
-// shapes' layouts, so the launch holds as much LDS per workgroup as the
-// largest shape alone.
+// the grid, [begin[s], end[s]), holds the items of shape s; the host chooses
+// the segments' order.  A workgroup of a shape with fewer than 8 waves ends
+// its other waves at once; the hardware barrier then waits only for the
+// waves still running.  The LDS is the union of the shapes' layouts, so the
+// launch holds as much LDS per workgroup as the largest shape alone.
 //
 // Shape s is FR_SHAPES[s] of the host plan: 0, 1, 2: 2, 4 and 8 waves of one
 // 32-row tile; 3, 4: the 16-row-tile kernel with 3 and 4 tiles per wave;

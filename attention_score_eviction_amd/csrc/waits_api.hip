@@ -404,8 +404,8 @@ static_assert(sizeof(FrMultiArgs) <= 4096, "kernel argument segment");
 
 // The few-rows launches of one pass: items[sh] work items on shape sh,
 // firsts[sh] the first item of each sequence among them.  Heads of several
-// shapes in a bf16 batch go into one few_rows_multi_kernel launch, the
-// row-block shape's segment first; otherwise each shape has its own launch.
+// shapes in a bf16 batch go into one few_rows_multi_kernel launch;
+// otherwise each shape has its own launch.
 template <bool PASS2>
 int launch_fr_shapes(const waits_shape* s, const FrArgs& f, const int* items,
                      const int32_t (*firsts)[MAXB + 1], hipStream_t st) {
@@ -416,7 +416,13 @@ int launch_fr_shapes(const waits_shape* s, const FrArgs& f, const int* items,
     std::memset(&m, 0, sizeof(m));
     m.f = f;
     int at = 0;
-    for (int sh = FR_NSHAPES - 1; sh >= 0; --sh) {
+    // few-rows heads first (largest shape first), the row blocks last: a
+    // sequence's row blocks run longest first, so the grid ends on the
+    // shortest items (1-2% faster than row blocks first on the 1B batch)
+    constexpr int order[FR_NSHAPES] = {4, 3, 2, 1, 0, 5};
+    static_assert(order[FR_NSHAPES - 1] == FR_BIG_SHAPE, "row blocks last");
+    for (int o = 0; o < FR_NSHAPES; ++o) {
+      const int sh = order[o];
       m.begin[sh] = at;
       at += items[sh];
       m.end[sh] = at;
