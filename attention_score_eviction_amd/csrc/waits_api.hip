@@ -22,9 +22,9 @@
 #include "select_wide.hpp"
 #include "attention.hpp"
 
-// Scratch of waits_select_compact_noalloc (the wide select's digit
-// histograms and per-chunk counts), one copy per GPU for the life of the
-// process.  In host code `scratch` is a host-side stand-in, not a device
+// Scratch of waits_select_compact_noalloc (the wide select's per-chunk digit
+// histograms and counts and per-head picks), one copy per GPU for the life
+// of the process.  In host code `scratch` is a host-side stand-in, not a device
 // address: kernels get the address hipGetSymbolAddress reports for their
 // device (device_scratch below).
 constexpr size_t STATIC_SCRATCH_BYTES = WAITS_STATIC_SCRATCH_BYTES;
@@ -735,12 +735,15 @@ void fill_len_table(SeqTable& t, const waits_shape* s, int lo, int hi) {
   }
 }
 
-// Workspace of the several-workgroup select for sequences [lo, hi): the
-// per-(sequence, head) digit histograms, then one (above, equal) count pair
-// per chunk.  0 when every sequence is short enough for one workgroup.
+// Workspace of the several-workgroup select for sequences [lo, hi): per
+// chunk its two 16-bit digit histograms (1 KiB), then per chunk its counts
+// above the first three picks (16 bytes), then per (sequence, head) the
+// four (prefix, keys still to keep) pairs (32 bytes).  0 when every
+// sequence is short enough for one workgroup.
 struct WideWs {
-  size_t hist_bytes = 0, count_bytes = 0;
+  size_t hist_bytes = 0, above_bytes = 0, state_bytes = 0;
   int items = 0;
+  size_t total() const { return hist_bytes + above_bytes + state_bytes; }
 };
 WideWs wide_ws(const waits_shape* s, int lo, int hi) {
   WideWs w;
@@ -748,17 +751,15 @@ WideWs wide_ws(const waits_shape* s, int lo, int hi) {
   for (int i = lo; i < hi; ++i) gmax = std::max(gmax, seq_len(s, i));
   if (gmax <= SEL_WIDE_MIN) return w;
   for (int i = lo; i < hi; ++i) w.items += s->n_kv_heads * wide_chunks(seq_len(s, i));
-  w.hist_bytes = (size_t)(hi - lo) * s->n_kv_heads * 4 * 256 * sizeof(int);
-  w.count_bytes = (size_t)w.items * sizeof(int2);
+  w.hist_bytes = (size_t)w.items * WIDE_HIST_BYTES;
+  w.above_bytes = (size_t)w.items * sizeof(int4);
+  w.state_bytes = (size_t)(hi - lo) * s->n_kv_heads * 4 * sizeof(int2);
   return w;
 }
 
 size_t select_ws_bytes(const waits_shape* s) {
   size_t mx = 0;
-  for (int lo = 0; lo < s->batch; lo += MAXB) {
-    const WideWs w = wide_ws(s, lo, std::min(s->batch, lo + MAXB));
-    mx = std::max(mx, w.hist_bytes + w.count_bytes);
-  }
+  for (int lo = 0; lo < s->batch; lo += MAXB) mx = std::max(mx, wide_ws(s, lo, std::min(s->batch, lo + MAXB)).total());
   return mx;
 }
 
@@ -807,8 +808,9 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
       std::memset(&args, 0, sizeof(args));
       args.scores = scores;
       args.idx = idx + first_row;
-      args.hist = static_cast<int*>(ws);
-      args.counts = reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.hist_bytes);
+      args.chist = static_cast<uint16_t*>(ws);
+      args.above = reinterpret_cast<int4*>(static_cast<unsigned char*>(ws) + w.hist_bytes);
+      args.state = reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.hist_bytes + w.above_bytes);
       args.T = s->cu_seqlens[s->batch];
       args.hkv = s->n_kv_heads;
       args.budget = budget;
@@ -826,18 +828,12 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
         items += s->n_kv_heads * wide_chunks(seq_len(s, i));
       }
       args.tab.first[hi - lo] = items;
-      const int64_t words = (int64_t)(w.hist_bytes / sizeof(int));
-      hipLaunchKernelGGL(wide_zero_kernel, dim3((unsigned)std::min<int64_t>(1024, (words + 255) / 256)),
-                         dim3(256), 0, stream, args.hist, words);
-      if (launched() != WAITS_OK) return WAITS_EDEVICE;
       if (items > 0) {
         for (int d = 0; d < 4; ++d) {
           args.digit = d;
           hipLaunchKernelGGL(wide_hist_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
           if (launched() != WAITS_OK) return WAITS_EDEVICE;
         }
-        hipLaunchKernelGGL(wide_count_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
-        if (launched() != WAITS_OK) return WAITS_EDEVICE;
         hipLaunchKernelGGL((wide_emit_kernel<FUSE>), dim3(items), dim3(SEL_THREADS), 0, stream, args);
         if (launched() != WAITS_OK) return WAITS_EDEVICE;
       }

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_PKG, "libwaits.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "waits.h")
 
 WAITS_OK, WAITS_EINVAL, WAITS_EUNSUPPORTED, WAITS_EWORKSPACE, WAITS_EDEVICE, WAITS_ESCRATCH = range(6)
-STATIC_SCRATCH_BYTES = 4 << 20   # WAITS_STATIC_SCRATCH_BYTES
+STATIC_SCRATCH_BYTES = 16 << 20  # WAITS_STATIC_SCRATCH_BYTES
 WAITS_BF16, WAITS_F32 = 0, 1
 WAITS_PASS2_AUTO, WAITS_PASS2_KEY_BLOCKS = 0, 1
 _PASS2 = {"auto": WAITS_PASS2_AUTO, "key_blocks": WAITS_PASS2_KEY_BLOCKS}

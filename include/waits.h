@@ -199,8 +199,8 @@ int waits_select(const waits_shape* shape, const float* scores,
 /*
  * Bytes of device workspace waits_select and waits_select_compact need for
  * this batch: 0 unless a sequence has more than 32768 keys, whose selection
- * is split over several workgroups that meet in the workspace (per-head digit
- * histograms and per-chunk counts).  workspace: device, 16-byte aligned.
+ * is split over several workgroups that meet in the workspace (per-chunk digit
+ * histograms and counts, per-head picks).  workspace: device, 16-byte aligned.
  */
 int waits_select_workspace_bytes(const waits_shape* shape, int32_t select_budget,
                                  size_t* bytes);
@@ -237,23 +237,24 @@ int waits_select_compact(const waits_shape* shape, const float* scores,
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): no workspace argument, and the same outputs, layouts and
  * error codes as waits_select_compact, bit for bit.  The select of heads of
- * more than 32768 keys needs scratch (digit histograms and per-chunk counts:
- * the bytes waits_select_workspace_bytes reports); this call takes it from a
- * static device array of WAITS_STATIC_SCRATCH_BYTES that the library holds
- * on every GPU it runs on until the process ends, and returns WAITS_ESCRATCH
- * for a batch that needs more: a launch group (32 sequences) with such a
- * head needs 4 KiB per (sequence, KV head) plus 8 bytes per 4096 keys of
- * each head, e.g. 1.1 MiB for 32 sequences x 8 KV heads of 131072 keys.
+ * more than 32768 keys needs scratch (per-chunk digit histograms and counts,
+ * per-head picks: the bytes waits_select_workspace_bytes reports); this call
+ * takes it from a static device array of WAITS_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, and returns
+ * WAITS_ESCRATCH for a batch that needs more: a launch group (32 sequences)
+ * with such a head needs 1040 bytes per 4096 keys of each head plus 32 bytes
+ * per (sequence, KV head), e.g. 8.5 MiB for 32 sequences x 8 KV heads of
+ * 131072 keys.
  * - The scratch of a GPU is the copy on the device `stream` belongs to (the
  *   current device for the null stream); the first call for a device looks
  *   its address up (hipGetSymbolAddress) and keeps it.
  * - Every call on a GPU shares that GPU's array and leaves its contents
- *   behind; each call clears what it needs before use.  Calls that overlap
+ *   behind; each call writes every word it reads before reading it.  Calls that overlap
  *   on one GPU (several streams or host threads at once) race on the array
  *   and give undefined results: serialise them.
  * - No device or host memory is allocated by this call.
  */
-#define WAITS_STATIC_SCRATCH_BYTES (4u << 20)
+#define WAITS_STATIC_SCRATCH_BYTES (16u << 20)
 int waits_select_compact_noalloc(const waits_shape* shape, const float* scores,
                                  const void* k, const void* v, int32_t select_budget,
                                  int32_t* idx, void* k_out, void* v_out, hipStream_t stream);

@@ -174,9 +174,10 @@ def test_select_workspace():
     # one workgroup per (sequence, head) up to 32768 keys: no workspace
     assert W.select_workspace_bytes([0, 32768], 8, 128) == 0
     assert W.select_workspace_bytes([0, 0], 8, 128) == 0
-    # longer: 4096-key chunks; histograms [seq, head, 4, 256] int32 + a count pair per chunk
+    # longer: 4096-key chunks; per chunk two 256-bin uint16 histograms and an
+    # int4 of counts, then per (sequence, head) four (prefix, keys left) pairs
     need = W.select_workspace_bytes([0, 131072, 131072 + 5000], 8, 2048)
-    assert need == 2 * 8 * 4 * 256 * 4 + 8 * (32 + 2) * 8
+    assert need == 8 * (32 + 2) * (2 * 256 * 2 + 16) + 2 * 8 * 4 * 8
     s = _shape(cu=[0, 40000], hkv=2)
     lib = W.lib()
     assert lib.waits_select(ctypes.byref(s), FAKE, 64, FAKE, None, 0, None) == W.WAITS_EWORKSPACE
@@ -341,11 +342,11 @@ def test_decode_binding_checks_layouts():
 
 
 def test_noalloc_select_compact_rejects_batches_beyond_its_scratch():
-    # 32 sequences x 32 KV heads of 40000 keys: 4 MiB of digit histograms plus
-    # the per-chunk counts pass the static scratch; refused before any launch
+    # 32 sequences x 32 KV heads of 80000 keys: 20 chunks per head of 1040
+    # bytes each (21 MB) pass the 16 MiB static scratch; refused before any launch
     lib = W.lib()
     assert "scratch" in W.strerror(W.WAITS_ESCRATCH)
-    s = _shape(cu=[40000 * i for i in range(33)], hkv=32, hq=32)
+    s = _shape(cu=[80000 * i for i in range(33)], hkv=32, hq=32)
     need = ctypes.c_size_t(0)
     assert lib.waits_select_workspace_bytes(ctypes.byref(s), 256, ctypes.byref(need)) == 0
     assert need.value > W.STATIC_SCRATCH_BYTES

@@ -598,11 +598,13 @@ def test_select_segment_boundaries(n):
             np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
 
 
-@pytest.mark.parametrize("n", [129, 1000, 5000, 16383, 20001, 32767])
+@pytest.mark.parametrize("n", [129, 1000, 5000, 16383, 20001, 32767, 40001, 70000])
 def test_select_threshold_zero(n):
     # fewer positive scores than the budget: the kept zeros are the
     # lowest-positioned ones (the kernel's slots past N also read as 0 and
-    # must never be kept); one head all zeros, one with 40 positives
+    # must never be kept); one head all zeros, one with 40 positives.  Past
+    # 32768 keys the select runs over several workgroups, where the kept
+    # zeros come from the first chunk and the positives from any
     _say(f"select threshold 0 n={n}")
     rng = np.random.default_rng(2000 + n)
     s = np.zeros((2, n), dtype=np.float32)
