@@ -40,14 +40,16 @@ struct IntC {
   static constexpr int value = V;
 };
 
-// LDS of the 16-row-tile workgroup (8 waves, NT tiles each; 4 sub-tiles per stage).
+constexpr int FR16_SUB = 4;  // 32-key sub-tiles per stage of the 16-row-tile kernel
+
+// LDS of the 16-row-tile workgroup (8 waves, NT tiles each).
 template <int D, int NT>
 struct Fr16Lds {
   static constexpr int ROWS = 8 * NT * 16;
-  alignas(16) unsigned char lds[2][4][TileGeom<bf16_t, D>::LDS_BYTES];  // K double buffer
+  alignas(16) unsigned char lds[2][FR16_SUB][TileGeom<bf16_t, D>::LDS_BYTES];  // K double buffer
   alignas(16) float row_off[ROWS];
   alignas(16) int row_q[ROWS];
-  alignas(16) float red[2 * 4][8][2 * TILE];  // key k: [2k], [2k + 1]
+  alignas(16) float red[2 * FR16_SUB][8][2 * TILE];  // key k: [2k], [2k + 1]
 };
 
 // One work item (index `item` among the items of `first`) on the whole
@@ -64,7 +66,7 @@ __device__ __forceinline__ void few_rows16_body(const FrArgs& args, const int32_
   static_assert(ROWS <= FR_ROWS, "at most FR_ROWS rows per workgroup");
   constexpr int KS = D / 32;                                 // MFMA steps per 16x16 tile
   constexpr int CPR = Geo::ROW_BYTES / 16;                   // 16-byte chunks per K row
-  constexpr int FR_SUB = 4;                                  // 32-key sub-tiles per stage
+  constexpr int FR_SUB = FR16_SUB;
   constexpr int FR_STAGE = FR_SUB * TILE;
   constexpr int CHUNKS = FR_STAGE * CPR;
   constexpr int SV = (CHUNKS + FR_THREADS - 1) / FR_THREADS;
