@@ -69,6 +69,13 @@ constexpr FrShape FR_SHAPES[] = {{64, 2, 1, 0},  {128, 4, 1, 0}, {256, 8, 1, 0},
 constexpr int FR_NSHAPES = 6;
 constexpr int FR_BIG_SHAPE = FR_NSHAPES - 1;
 static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the largest shape");
+// Pass 1 of bf16 head_dim 64 runs its row blocks on the one-tile 8-wave shape
+// (256 rows): about 110 VGPRs, so two workgroups share a CU, and the
+// VALU-bound epilogue (one exponential per 64-term dot product) has twice
+// the waves to interleave.  Pass 2 keeps 512-row blocks: its per-block
+// column sums would double on 256-row blocks.
+constexpr int FR_P1_SHAPE64 = 2;
+static_assert(FR_SHAPES[FR_P1_SHAPE64].waves == 8 && FR_SHAPES[FR_P1_SHAPE64].tiles == 1, "shape table");
 
 // How a sequence's two passes run.
 enum class Mode {
@@ -164,17 +171,18 @@ int64_t group_span(const waits_shape* s) {
   return ((int64_t)(G - 1) * s->q_stride_head + s->head_dim) * e;
 }
 
-// Launch plan.  A sequence whose packed rows fit one workgroup per KV head
-// runs both passes on the few-rows kernel, its key range cut into chunks
-// until the batch has about one workgroup per compute unit.  A longer one
-// runs pass 1 on the same kernel in row blocks (key chunks for balance).  Its
-// pass 2 runs on the same row blocks and key chunks, each block writing its
+// Launch plan of pass 1 or pass 2.  A sequence whose packed rows fit one
+// workgroup per KV head runs both passes on the few-rows kernel, its key
+// range cut into chunks until the batch has about one workgroup per compute
+// unit.  A longer one runs pass 1 on the same kernel in row blocks (512 rows;
+// 256 for bf16 head_dim 64) with key chunks for balance.  Its pass 2 runs on
+// 512-row blocks with key chunks planned the same way, each block writing its
 // column sums for a fixed-order reduce, while the partials stay under
 // RB_PART_MAX per sequence and RB_PART_TOTAL per launch group; other long
 // sequences run pass 2 on key blocks (row chunks for balance), whose partials
 // are [row chunk][Hkv][T].  Every chunk a buffer load
 // addresses spans less than 2^31 bytes.
-std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b) {
+std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* b, int pass) {
   const int G = s->n_q_heads / s->n_kv_heads;
   const int hkv = s->n_kv_heads;
   const bool fr_ok = !(s->dtype == WAITS_F32 && s->head_dim == 128);
@@ -207,7 +215,8 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       fr_units += (int64_t)hkv * FR_SHAPES[q.frs].waves;
     } else {
       q.mode = Mode::BIG;
-      q.nrb = (q.pr + FR_ROWS - 1) / FR_ROWS;
+      q.frs = pass == 1 && s->head_dim == 64 && s->dtype == WAITS_BF16 ? FR_P1_SHAPE64 : FR_BIG_SHAPE;
+      q.nrb = (q.pr + FR_SHAPES[q.frs].rows - 1) / FR_SHAPES[q.frs].rows;
       q.nkb = (q.n + KB_KEYS - 1) / KB_KEYS;
       big_units1 += (int64_t)hkv * q.nrb;
       big_units2 += (int64_t)hkv * q.nkb;
@@ -408,7 +417,7 @@ static_assert(sizeof(FrMultiArgs) <= 4096, "kernel argument segment");
 // otherwise each shape has its own launch.
 template <bool PASS2>
 int launch_fr_shapes(const waits_shape* s, const FrArgs& f, const int* items,
-                     const int32_t (*firsts)[MAXB + 1], hipStream_t st) {
+                     const int32_t (*firsts)[MAXB + 1], int rb_shape, hipStream_t st) {
   int active = 0;
   for (int sh = 0; sh < FR_NSHAPES; ++sh) active += items[sh] > 0 ? 1 : 0;
   if (s->dtype == WAITS_BF16 && active > 1) {
@@ -416,11 +425,14 @@ int launch_fr_shapes(const waits_shape* s, const FrArgs& f, const int* items,
     std::memset(&m, 0, sizeof(m));
     m.f = f;
     int at = 0;
-    // few-rows heads first (largest shape first), the row blocks last: a
-    // sequence's row blocks run longest first, so the grid ends on the
-    // shortest items (1-2% faster than row blocks first on the 1B batch)
-    constexpr int order[FR_NSHAPES] = {4, 3, 2, 1, 0, 5};
-    static_assert(order[FR_NSHAPES - 1] == FR_BIG_SHAPE, "row blocks last");
+    // few-rows heads first (largest shape first), the row blocks (shape
+    // rb_shape) last: a sequence's row blocks run longest first, so the grid
+    // ends on the shortest items (1-2% faster than row blocks first on the
+    // 1B batch)
+    int order[FR_NSHAPES], no = 0;
+    for (int sh = FR_NSHAPES - 1; sh >= 0; --sh)
+      if (sh != rb_shape) order[no++] = sh;
+    order[no++] = rb_shape;
     for (int o = 0; o < FR_NSHAPES; ++o) {
       const int sh = order[o];
       m.begin[sh] = at;
@@ -460,7 +472,7 @@ FrArgs fr_args(const waits_shape* s, const void* q, const void* k) {
 
 int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, const int32_t* b,
             float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const std::vector<Seq> v = plan_seqs(s, a, b);
+  const std::vector<Seq> v = plan_seqs(s, a, b, 1);
   if (ws_bytes < lse_ws_bytes(s, v) || (lse_ws_bytes(s, v) > 0 && !ws)) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;
   const int hkv = s->n_kv_heads;
@@ -485,7 +497,8 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
         }
         firsts[shape][hi - lo] = items[shape];
       }
-      if (launch_fr_shapes<false>(s, f, items, firsts, stream) != WAITS_OK) return WAITS_EDEVICE;
+      const int rb_shape = s->head_dim == 64 && s->dtype == WAITS_BF16 ? FR_P1_SHAPE64 : FR_BIG_SHAPE;
+      if (launch_fr_shapes<false>(s, f, items, firsts, rb_shape, stream) != WAITS_OK) return WAITS_EDEVICE;
     }
 
     // fp32 rows of head_dim 128
@@ -554,7 +567,7 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
 int run_colsum(const waits_shape* s, const void* q, const void* k, const float* lse,
                const float* a, const int32_t* b, float* scores, void* ws, size_t ws_bytes,
                hipStream_t stream) {
-  const std::vector<Seq> v = plan_seqs(s, a, b);
+  const std::vector<Seq> v = plan_seqs(s, a, b, 2);
   // only the key-block kernel addresses a group's Q rows from one buffer base
   for (const Seq& sq : v)
     if (sq.mode == Mode::BIG && !sq.p2rb && group_span(s) > SPAN_BYTES / 2) return WAITS_EUNSUPPORTED;
@@ -593,7 +606,7 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
         }
         firsts[shape][hi - lo] = items[shape];
       }
-      if (launch_fr_shapes<true>(s, f, items, firsts, stream) != WAITS_OK) return WAITS_EDEVICE;
+      if (launch_fr_shapes<true>(s, f, items, firsts, FR_BIG_SHAPE, stream) != WAITS_OK) return WAITS_EDEVICE;
     }
     {
       RowBlockReduceArgs ra;
@@ -1004,7 +1017,7 @@ int waits_lse_workspace_bytes(const waits_shape* s, const float* a, const int32_
   if (rc == WAITS_OK) rc = check_curves(s, a, b);
   if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
   if (rc != WAITS_OK) return rc;
-  *bytes = lse_ws_bytes(s, plan_seqs(s, a, b));
+  *bytes = lse_ws_bytes(s, plan_seqs(s, a, b, 1));
   return WAITS_OK;
 }
 
@@ -1014,7 +1027,7 @@ int waits_colsum_workspace_bytes(const waits_shape* s, const float* a, const int
   if (rc == WAITS_OK) rc = check_curves(s, a, b);
   if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
   if (rc != WAITS_OK) return rc;
-  *bytes = colsum_ws_bytes(s, plan_seqs(s, a, b));
+  *bytes = colsum_ws_bytes(s, plan_seqs(s, a, b, 2));
   return WAITS_OK;
 }
 
@@ -1024,8 +1037,8 @@ int waits_score_workspace_bytes(const waits_shape* s, const float* a, const int3
   if (rc == WAITS_OK) rc = check_curves(s, a, b);
   if (rc == WAITS_OK && !bytes) rc = WAITS_EINVAL;
   if (rc != WAITS_OK) return rc;
-  const std::vector<Seq> v = plan_seqs(s, a, b);
-  *bytes = lse_buffer_bytes(s) + std::max(lse_ws_bytes(s, v), colsum_ws_bytes(s, v));
+  *bytes = lse_buffer_bytes(s) +
+           std::max(lse_ws_bytes(s, plan_seqs(s, a, b, 1)), colsum_ws_bytes(s, plan_seqs(s, a, b, 2)));
   return WAITS_OK;
 }
 
@@ -1061,9 +1074,9 @@ int waits_score(const waits_shape* s, const void* q, const void* k, const float*
   if (s->cu_seqlens[s->batch] == 0) return WAITS_OK;
   if (!q || !k || !scores || !is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(scores, 4))
     return WAITS_EINVAL;
-  const std::vector<Seq> v = plan_seqs(s, a, b);
   const size_t lse_bytes = lse_buffer_bytes(s);
-  const size_t need = lse_bytes + std::max(lse_ws_bytes(s, v), colsum_ws_bytes(s, v));
+  const size_t need =
+      lse_bytes + std::max(lse_ws_bytes(s, plan_seqs(s, a, b, 1)), colsum_ws_bytes(s, plan_seqs(s, a, b, 2)));
   if (!ws || ws_bytes < need || !is_aligned(ws, 256)) return WAITS_EWORKSPACE;
   float* lse = static_cast<float*>(ws);
   void* part = static_cast<unsigned char*>(ws) + lse_bytes;  // pass-1 partials, then pass-2 partials
