@@ -70,10 +70,10 @@ constexpr int FR_NSHAPES = 6;
 constexpr int FR_BIG_SHAPE = FR_NSHAPES - 1;
 static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the largest shape");
 // Pass 1 of bf16 head_dim 64 runs its row blocks on the one-tile 8-wave shape
-// (256 rows): about 110 VGPRs, so two workgroups share a CU, and the
-// VALU-bound epilogue (one exponential per 64-term dot product) has twice
-// the waves to interleave.  Pass 2 keeps 512-row blocks: its per-block
-// column sums would double on 256-row blocks.
+// (256 rows): twice the blocks, so a batch needs fewer key splits (and
+// partials) for balance, and the shape's own kernel (about 110 VGPRs) fits
+// two workgroups per CU.  Measured 5-8% faster than 512-row blocks.  Pass 2
+// keeps 512-row blocks: its per-block column sums would double.
 constexpr int FR_P1_SHAPE64 = 2;
 static_assert(FR_SHAPES[FR_P1_SHAPE64].waves == 8 && FR_SHAPES[FR_P1_SHAPE64].tiles == 1, "shape table");
 
