@@ -409,6 +409,24 @@ def test_ragged_small_sizes(n, hq, hkv, d):
         _full_check(bt, [a], [b], 64)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_workgroup_shape_in_one_batch(d):
+    # packed rows per KV head (G = 4): a = 0 -> 12000 (row blocks), a = 10
+    # with b = 1 / 16 / 40 -> 40 / 100 / 196 (the 2-, 4- and 8-wave one-tile
+    # shapes), a = 1 with b = 16 / 1 -> 420 / 360 (the 16-row-tile bodies with
+    # 4 and 3 tiles per wave), a = inf with b = 128 -> 512 (the two-tile
+    # shape).  Each pass runs all of them in one launch; at head_dim 64 pass
+    # 1's 256-row blocks share a segment with the 196-row heads.
+    lengths = [3000, 1800, 2200, 2500, 2600, 2100, 1900]
+    a = [0.0, 10.0, 10.0, 10.0, 1.0, 1.0, math.inf]
+    b = [1, 1, 16, 40, 16, 1, 128]
+    _say(f"every shape in one batch d={d}")
+    bt = make_batch([140 + i for i in range(len(lengths))], lengths, 8, 2, d, heavy=True)
+    first = W.waits.first_rows(bt.cu_seqlens, a, b)
+    assert [4 * (n - int(f)) for n, f in zip(lengths, first)] == [12000, 40, 100, 196, 420, 360, 512]
+    _full_check(bt, a, b, 128)
+
+
 @pytest.mark.parametrize("scale", [0.05, 0.3])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_softmax_scale_other_than_default(scale, dtype):
