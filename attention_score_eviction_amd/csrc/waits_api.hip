@@ -77,6 +77,11 @@ static_assert(FR_SHAPES[FR_BIG_SHAPE].rows == FR_ROWS, "row blocks use the large
 constexpr int FR_P1_SHAPE64 = 2;
 static_assert(FR_SHAPES[FR_P1_SHAPE64].waves == 8 && FR_SHAPES[FR_P1_SHAPE64].tiles == 1, "shape table");
 
+// The workgroup shape of row blocks (heads of more than FR_ROWS packed rows) in pass 1 or 2.
+int row_block_shape(const waits_shape* s, int pass) {
+  return pass == 1 && s->head_dim == 64 && s->dtype == WAITS_BF16 ? FR_P1_SHAPE64 : FR_BIG_SHAPE;
+}
+
 // How a sequence's two passes run.
 enum class Mode {
   NONE,   // no tokens
@@ -215,7 +220,7 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       fr_units += (int64_t)hkv * FR_SHAPES[q.frs].waves;
     } else {
       q.mode = Mode::BIG;
-      q.frs = pass == 1 && s->head_dim == 64 && s->dtype == WAITS_BF16 ? FR_P1_SHAPE64 : FR_BIG_SHAPE;
+      q.frs = row_block_shape(s, pass);
       q.nrb = (q.pr + FR_SHAPES[q.frs].rows - 1) / FR_SHAPES[q.frs].rows;
       q.nkb = (q.n + KB_KEYS - 1) / KB_KEYS;
       big_units1 += (int64_t)hkv * q.nrb;
@@ -497,8 +502,8 @@ int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, 
         }
         firsts[shape][hi - lo] = items[shape];
       }
-      const int rb_shape = s->head_dim == 64 && s->dtype == WAITS_BF16 ? FR_P1_SHAPE64 : FR_BIG_SHAPE;
-      if (launch_fr_shapes<false>(s, f, items, firsts, rb_shape, stream) != WAITS_OK) return WAITS_EDEVICE;
+      if (launch_fr_shapes<false>(s, f, items, firsts, row_block_shape(s, 1), stream) != WAITS_OK)
+        return WAITS_EDEVICE;
     }
 
     // fp32 rows of head_dim 128
@@ -606,7 +611,8 @@ int run_colsum(const waits_shape* s, const void* q, const void* k, const float* 
         }
         firsts[shape][hi - lo] = items[shape];
       }
-      if (launch_fr_shapes<true>(s, f, items, firsts, FR_BIG_SHAPE, stream) != WAITS_OK) return WAITS_EDEVICE;
+      if (launch_fr_shapes<true>(s, f, items, firsts, row_block_shape(s, 2), stream) != WAITS_OK)
+        return WAITS_EDEVICE;
     }
     {
       RowBlockReduceArgs ra;
