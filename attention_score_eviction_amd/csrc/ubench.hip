@@ -125,6 +125,121 @@ int run_mode(int threads, int blocks, int iters, float* out, long long* stamps, 
   return 0;
 }
 
+// The passes' own shape at NT = 4 row tiles (head_dim 128): per iteration a
+// wave issues 32 MFMAs (8 accumulators x 4 head-dim steps) into acc[par]
+// and the epilogue of acc[par ^ 1] (32 elements per lane: fma, exp2, add
+// into four row sums), the two pinned into groups of G MFMAs followed by
+// 3 G VALU instructions (G = 32: one cluster, as the kernels issue them).
+// TM_MFMA and TM_EPI run only one of the two streams.
+enum TileMode { TM_MFMA = 0, TM_EPI = 1, TM_MIX = 2 };
+
+template <int TM, int G, int PRIO>
+__global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps, int iters, float c) {
+  static_assert(G >= 1 && G <= 32 && 32 % G == 0, "G divides 32");
+  const int tid = threadIdx.x;
+  bf16x8 a[4], b[2][4];
+  for (int s = 0; s < 4; ++s)
+    for (int i = 0; i < 8; ++i) {
+      a[s][i] = (__bf16)(0.001f * (tid + i + s));
+      b[0][s][i] = (__bf16)(0.002f * (tid - i + s));
+      b[1][s][i] = (__bf16)(0.003f * (tid - i - s));
+    }
+  f32x4 acc[2][8];
+  for (int p = 0; p < 2; ++p)
+    for (int m = 0; m < 8; ++m) acc[p][m] = f32x4{0.01f * m, 0.f, 0.f, 0.f};
+  float m4[4] = {0.1f, 0.2f, 0.3f, 0.4f}, sum[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      if constexpr (TM != TM_EPI) {
+        // opaque operands: the two parities' MFMAs are not merged or hoisted
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          asm volatile("" : "+v"(b[0][s]));
+          asm volatile("" : "+v"(b[1][s]));
+        }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const int m = t * 2 + kt;
+              acc[par][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  b[kt][s], a[t], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[par][m], 0, 0, 0);
+            }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) asm volatile("" : "+v"(acc[par ^ 1][m]));
+      }
+      if constexpr (TM != TM_MFMA) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float sv = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[par ^ 1][t * 2 + kt][i], c, -m4[t]));
+            sv += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          }
+          sum[t] += sv;
+        }
+      }
+      if constexpr (TM == TM_MIX) {
+        if constexpr (G < 32) {
+#pragma unroll
+          for (int g = 0; g < 32 / G; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);      // G MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 3 * G, 0);  // then 3 G VALU
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 96, 0);
+        }
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  float r = 0.f;
+  for (int p = 0; p < 2; ++p)
+    for (int m = 0; m < 8; ++m) r += acc[p][m][0] + acc[p][m][3];
+  for (int t = 0; t < 4; ++t) r += sum[t];
+  out[blockIdx.x * blockDim.x + tid] = r;
+  if ((tid & 63) == 0) {
+    const int w = blockIdx.x * (blockDim.x >> 6) + (tid >> 6);
+    stamps[2 * w] = t1 - t0;
+    stamps[2 * w + 1] = r1 - r0;
+  }
+}
+
+// res[0] = cycles per iteration (32 MFMAs and/or 32 epilogue elements per
+// wave) of the slowest wave, res[1] = shader clock in GHz.
+template <int TM, int G, int PRIO>
+int run_tile(int threads, int blocks, int iters, float* out, long long* stamps, double* res) {
+  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO>), dim3(blocks), dim3(threads), 0, 0, out, stamps, 16, 1.0001f);
+  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO>), dim3(blocks), dim3(threads), 0, 0, out, stamps, iters, 1.0001f);
+  if (hipDeviceSynchronize() != hipSuccess) return 4;
+  const int waves = blocks * (threads / 64);
+  std::vector<long long> h((size_t)waves * 2);
+  if (hipMemcpy(h.data(), stamps, sizeof(long long) * h.size(), hipMemcpyDeviceToHost) != hipSuccess) return 4;
+  long long mx = 0, rt = 0;
+  for (int w = 0; w < waves; ++w) {
+    mx = std::max(mx, h[2 * w]);
+    rt = std::max(rt, h[2 * w + 1]);
+  }
+  res[0] = (double)mx / iters;
+  res[1] = (double)mx / ((double)rt / 100e6) / 1e9;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,5 +280,31 @@ int waits_ubench_mix(int threads, int blocks, int iters, double* res, int* simd)
 }
 
 int waits_ubench_modes(void) { return N_MODES; }
+
+// The passes' shape (tile_kernel) on `blocks` workgroups of `threads` (256
+// or 512) threads; configurations in order: MFMAs only, epilogue only, one
+// cluster at raised priority, then groups of G = 32, 16, 8, 4, 2, 1 MFMAs.
+// res[2 * i + {0, 1}] = cycles per iteration of the slowest wave, clock GHz.
+int waits_ubench_tile(int threads, int blocks, int iters, double* res) {
+  if (threads != 256 && threads != 512) return 1;
+  if (iters < 2 || iters % 2) return 1;
+  float* out = nullptr;
+  long long* stamps = nullptr;
+  if (hipMalloc(&out, sizeof(float) * blocks * threads) != hipSuccess) return 4;
+  if (hipMalloc(&stamps, sizeof(long long) * 2 * blocks * (threads / 64)) != hipSuccess) return 4;
+  int rc = 0;
+  rc = rc ? rc : run_tile<TM_MFMA, 32, 0>(threads, blocks, iters, out, stamps, res + 0);
+  rc = rc ? rc : run_tile<TM_EPI, 32, 0>(threads, blocks, iters, out, stamps, res + 2);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1>(threads, blocks, iters, out, stamps, res + 4);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 0>(threads, blocks, iters, out, stamps, res + 6);
+  rc = rc ? rc : run_tile<TM_MIX, 16, 0>(threads, blocks, iters, out, stamps, res + 8);
+  rc = rc ? rc : run_tile<TM_MIX, 8, 0>(threads, blocks, iters, out, stamps, res + 10);
+  rc = rc ? rc : run_tile<TM_MIX, 4, 0>(threads, blocks, iters, out, stamps, res + 12);
+  rc = rc ? rc : run_tile<TM_MIX, 2, 0>(threads, blocks, iters, out, stamps, res + 14);
+  rc = rc ? rc : run_tile<TM_MIX, 1, 0>(threads, blocks, iters, out, stamps, res + 16);
+  (void)hipFree(out);
+  (void)hipFree(stamps);
+  return rc;
+}
 
 }  // extern "C"

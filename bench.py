@@ -616,6 +616,9 @@ UBENCH_MODES = ["mfma: 8 MFMA 16x16x32 bf16", "triple: 8 (fma, exp, add)", "exp:
                 "clusters: 8 MFMA then 8 triples", "clusters, MFMA at raised wave priority",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 triples",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 fma", "split: waves 0-3 8 MFMA, waves 4-7 8 exp"]
+UBENCH_TILE = ["MFMAs only", "epilogue only", "one cluster, MFMAs at raised priority",
+               "groups of 32 MFMAs", "groups of 16", "groups of 8", "groups of 4", "groups of 2",
+               "groups of 1"]
 
 
 def ubench(args):
@@ -639,6 +642,17 @@ def ubench(args):
                                                        "waves_second_half": round(res[3 * i + 1], 1),
                                                        "clock_ghz": round(res[3 * i + 2], 3)}
                                                    for i, m in enumerate(UBENCH_MODES)}}), flush=True)
+    # the passes' own shape: 32 MFMAs and a 32-element epilogue per wave and iteration
+    for threads in (256, 512):
+        res = (ctypes.c_double * (2 * len(UBENCH_TILE)))()
+        rc = lib.waits_ubench_tile(threads, 256, 4000, res)
+        if rc:
+            raise SystemExit(f"waits_ubench_tile failed ({rc})")
+        print(json.dumps({"ubench": "pass shape (32 MFMA + 32 epilogue elements per wave)",
+                          "threads": threads, "workgroups": 256, "waves_per_simd": threads // 256,
+                          "cycles_per_iteration": {m: {"slowest_wave": round(res[2 * i], 1),
+                                                       "clock_ghz": round(res[2 * i + 1], 3)}
+                                                   for i, m in enumerate(UBENCH_TILE)}}), flush=True)
 
 
 def main():
