@@ -1,30 +1,37 @@
 // Top-k select for long key ranges (more keys than one workgroup handles
 // well): each (sequence, KV head) is cut into chunks of WIDE_CHUNK keys, one
-// workgroup each, and the same MSB-first radix select as select_kernel runs
-// over five launches that meet in a small workspace.  No launch clears
-// memory and no two workgroups write one word: every chunk writes its own
-// histograms and counts, and the next launch sums the head's chunks.
-//   wide_hist_kernel, digit 0   each chunk's histogram of the top byte;
-//   wide_hist_kernel, digit d   (d = 1, 2, 3) sums digit d - 1's chunk
-//                               histograms over the head, picks that digit
-//                               (every workgroup of the head finds the same),
-//                               stores the chunk's count of keys above the
-//                               pick, and writes the histogram of digit d of
-//                               its keys that match the d picked digits;
-//   wide_emit_kernel            picks the last digit the same way (threshold
-//                               T, and how many keys equal to T are kept),
-//                               then places its kept keys: slot = (kept keys
-//                               above T before it) + min(keys equal to T
-//                               before it, the T-equal keys kept), the
-//                               earlier chunks' part from their stored counts
-//                               and last-digit histograms, the own part from
-//                               wave ballots; optionally gathers its kept K/V
-//                               rows (bit copies).
-// Histograms hold 16-bit counts (a chunk has at most 4096 keys) in two
-// buffers per chunk: digit d goes to buffer d & 1, so the launch reading
-// digit d - 1 writes the other one.
-// Results equal select_kernel's bit for bit (ties to the lower position,
-// ascending output, -1 / zero rows past the kept count).
+// workgroup each, and the select runs in two launches that meet in the
+// workspace (WAITS README: the top-k selector of "Repository layout"; the
+// same order as select_kernel: bit patterns of the non-negative scores, ties
+// to the lower position).
+//
+//   wide_sort_kernel    each chunk counting-sorts its keys by the top 12 bits
+//                       of their order key (4096 bins, 1/16 of an octave):
+//                       it writes the bins' start offsets (and every 64th of
+//                       them again, contiguous) and its key positions in bin
+//                       order.  No atomics outside LDS, so the workspace
+//                       needs no initial state.
+//   wide_place_kernel   every chunk of a head reads all of the head's chunk
+//                       records: the counts at or above each 64th bin, then
+//                       at or above each bin of the one 64-bin group that
+//                       holds the budget-th largest key, give that key's bin
+//                       B and how many keys lie above it.  The keys of bin B
+//                       (few, as a rule) are read back through the sorted
+//                       positions, and three more radix digits over them
+//                       (bits 18-11, 10-3, 2-0) give the threshold T and how
+//                       many keys equal to T are kept.  Each chunk then
+//                       places its own kept keys, slot = (kept keys above T
+//                       before it) + min(keys equal to T before it, the
+//                       T-equal keys kept), the earlier chunks' part from
+//                       their records and bin-B keys, its own from wave
+//                       ballots, and optionally gathers their K/V rows.
+//
+// Every chunk of a head derives the same B and T from the same records.
+// Bin B's keys are held in LDS when they fit (WIDE_CACHE); past that (many
+// equal or nearly equal scores) each pass reads them again from the
+// workspace and the scores, which is slower but gives the same result.
+// Results equal select_kernel's bit for bit (ascending output, -1 / zero
+// rows past the kept count).
 #pragma once
 
 #include "device_common.hpp"
@@ -36,9 +43,24 @@ namespace waits {
 constexpr int WIDE_CHUNK = 4096;                       // keys per workgroup
 constexpr int WIDE_PER = WIDE_CHUNK / SEL_THREADS;     // keys per lane
 constexpr int WIDE_SEG = WIDE_PER * WAVE;              // keys per wave
-constexpr int WIDE_HIST_BYTES = 2 * 256 * 2;           // per chunk: two 256-bin uint16 histograms
-constexpr int WIDE_SUM_GROUPS = SEL_THREADS / 128;     // chunk groups of the cross-chunk sum
-static_assert(WIDE_CHUNK <= 65535, "16-bit histogram counts");
+constexpr int WIDE_BINS = 4096;                        // bins of the 12-bit key prefix
+constexpr int WIDE_SHIFT = 19;                         // order keys are 31 bits: prefix = bits 30..19
+constexpr int WIDE_GROUP = 64;                         // bins per coarse group
+constexpr int WIDE_GROUPS = WIDE_BINS / WIDE_GROUP;
+constexpr int WIDE_SUMS = SEL_THREADS / WIDE_GROUP;    // chunk groups of the cross-chunk sums
+constexpr int WIDE_MAX_CHUNKS = 1024;                  // chunks of the longest accepted head
+constexpr int WIDE_CACHE = 4096;                       // bin-B keys held in LDS
+// Chunk record: coarse offsets (u32, off[64 j] for j = 0..64), bin offsets
+// (u16, off[b] for b = 0..4096; off[4096] = the chunk's key count), key
+// positions in bin order (u16, relative to the chunk).
+constexpr int WREC_COARSE = 0;
+constexpr int WREC_OFF = 272;
+constexpr int WREC_POS = WREC_OFF + 2 * 4104;
+constexpr int WIDE_REC_BYTES = WREC_POS + 2 * WIDE_CHUNK;
+static_assert(WREC_OFF >= 4 * (WIDE_GROUPS + 1) && WREC_OFF % 16 == 0, "coarse offsets fit");
+static_assert(WREC_POS % 16 == 0 && WIDE_REC_BYTES % 16 == 0, "16-byte aligned record parts");
+static_assert(WIDE_CHUNK <= 65535, "16-bit offsets and positions");
+static_assert(WIDE_BINS == 4 * SEL_THREADS, "four bins per thread in the chunk's scan");
 
 // Chunks of a key range (an empty one still gets one: its workgroup writes
 // the -1 slots and zero rows).
@@ -49,14 +71,11 @@ __host__ __device__ constexpr int wide_chunks(int n) {
 struct WideArgs {
   const float* scores;        // [Hkv, T]
   int32_t* idx;               // this launch's slice [nb, Hkv, budget]
-  uint16_t* chist;            // workspace [items][2][256]: each chunk's digit histograms
-  int4* above;                // workspace [items]: each chunk's keys above picked digits 0, 1, 2
-  int2* state;                // workspace [nb * Hkv][4]: (prefix of the first d picks, keys still to keep)
+  unsigned char* rec;         // workspace [items][WIDE_REC_BYTES]: each chunk's record
   int64_t T;
   int32_t hkv;
   int32_t budget;
-  int32_t digit;              // wide_hist_kernel: 0 (top byte) .. 3
-  const unsigned char* k;     // gather (wide_emit_kernel<true>)
+  const unsigned char* k;     // gather (wide_place_kernel<true>)
   const unsigned char* v;
   unsigned char* k_out;       // this launch's slice [nb, Hkv, budget, d]
   unsigned char* v_out;
@@ -69,8 +88,8 @@ struct WideArgs {
 // Where a workgroup's chunk sits and what it loads.
 struct WideItem {
   int p, h, ch, nch, N, keep, c0, item0;  // item0: the work item of the head's chunk 0
-  __amdgpu_buffer_rsrc_t rs;  // the head's scores (loads past N read 0)
-  int2* state;                // the head's 4 (prefix, keys still to keep) pairs
+  const float* sc;            // the head's scores
+  __amdgpu_buffer_rsrc_t rs;  // the same (loads past N read 0)
 };
 
 __device__ __forceinline__ WideItem wide_item(const WideArgs& args) {
@@ -86,9 +105,8 @@ __device__ __forceinline__ WideItem wide_item(const WideArgs& args) {
   w.item0 = item - w.ch;
   w.keep = min(args.budget, w.N);
   w.c0 = w.ch * WIDE_CHUNK;
-  const float* sc = args.scores + (int64_t)w.h * args.T + tab.tok0[w.p];
-  w.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), 0, w.N * 4, BUFFER_RSRC_WORD3);
-  w.state = args.state + ((int64_t)w.p * args.hkv + w.h) * 4;
+  w.sc = args.scores + (int64_t)w.h * args.T + tab.tok0[w.p];
+  w.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w.sc), 0, w.N * 4, BUFFER_RSRC_WORD3);
   return w;
 }
 
@@ -105,128 +123,89 @@ __device__ __forceinline__ void wide_load(const WideItem& w, int wave, int lane,
   }
 }
 
-// The head's histogram of digit d (buffer d & 1 of every chunk) into tot[256]
-// and, with BEFORE, that of the chunks ahead of this one into bef[256].
-// Thread t adds bins 2 (t % 128) and 2 (t % 128) + 1 of chunks t / 128 + 8 j
-// with range-checked 32-bit loads (chunks past the head read 0, so eight
-// loads go out together); red holds the WIDE_SUM_GROUPS partial sums.  Ends
-// with a barrier.
-template <bool BEFORE>
-__device__ __forceinline__ void wide_sum(const WideArgs& args, const WideItem& w, int d, int* tot, int* bef,
-                                         int (*red)[2][256]) {
-  const int tid = threadIdx.x;
-  const int bp = tid & 127, grp = tid >> 7;
-  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-      args.chist + (int64_t)w.item0 * (WIDE_HIST_BYTES / 2), 0, w.nch * WIDE_HIST_BYTES, BUFFER_RSRC_WORD3);
-  const int off = (d & 1) * 512 + bp * 4;  // bytes: the bin pair inside a chunk's record
-  int t0 = 0, t1 = 0, b0 = 0, b1 = 0;
-  for (int c = grp; c < w.nch; c += 8 * WIDE_SUM_GROUPS) {
-    uint32_t x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      x[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(hr, (c + j * WIDE_SUM_GROUPS) * WIDE_HIST_BYTES + off,
-                                                            0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int lo = (int)(x[j] & 0xFFFFu), hi = (int)(x[j] >> 16);
-      t0 += lo;
-      t1 += hi;
-      if constexpr (BEFORE) {
-        const bool early = c + j * WIDE_SUM_GROUPS < w.ch;
-        b0 += early ? lo : 0;
-        b1 += early ? hi : 0;
-      }
-    }
-  }
-  red[grp][0][2 * bp] = t0;
-  red[grp][0][2 * bp + 1] = t1;
-  if constexpr (BEFORE) {
-    red[grp][1][2 * bp] = b0;
-    red[grp][1][2 * bp + 1] = b1;
-  }
+// Exclusive prefix of x over the workgroup (thread order) and the total.
+// wsum: SEL_WAVES words; starts and ends with a barrier.
+__device__ __forceinline__ int block_excl_scan(int x, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  if (tid < 256) {
-    int s = 0, sb = 0;
-#pragma unroll
-    for (int g = 0; g < WIDE_SUM_GROUPS; ++g) {
-      s += red[g][0][tid];
-      if constexpr (BEFORE) sb += red[g][1][tid];
-    }
-    tot[tid] = s;
-    if constexpr (BEFORE) bef[tid] = sb;
-  }
+  const int incl = wave_incl_scan(x);
+  if (lane == WAVE - 1) wsum[wave] = incl;
   __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < SEL_WAVES; ++k) {
+    const int v = wsum[k];
+    base += k < wave ? v : 0;
+    tot += v;
+  }
+  total = tot;
+  __syncthreads();
+  return base + incl - x;
 }
 
 __global__ void __launch_bounds__(SEL_THREADS)
-wide_hist_kernel(const WideArgs args) {
-  __shared__ __attribute__((aligned(16))) int sub[256 * SEL_SUB];
-  __shared__ int red[WIDE_SUM_GROUPS][2][256];
-  __shared__ int tot[256];
-  __shared__ int lhist[256];
-  __shared__ int wabove[SEL_WAVES];
+wide_sort_kernel(const WideArgs args) {
+  __shared__ __attribute__((aligned(16))) int cnt[WIDE_BINS];
+  __shared__ int wsum[SEL_WAVES];
+  __shared__ __attribute__((aligned(16))) uint16_t spos[WIDE_CHUNK];
   const WideItem w = wide_item(args);
-  if (w.keep == w.N) return;  // every key is kept: nothing to select
+  if (w.keep == w.N) return;  // every key is kept: the place kernel reads no record
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int d = args.digit;
   uint32_t u[WIDE_PER];
   bool ok[WIDE_PER];
   wide_load(w, wave, lane, u, ok);
-  uint16_t* mine = args.chist + (int64_t)blockIdx.x * (WIDE_HIST_BYTES / 2) + (d & 1) * 256;
-  if (d == 0) {
-    // the top digit is shared by almost every key: per-(digit, lane % 32) words
-    for (int i = tid; i < 256 * SEL_SUB / 4; i += SEL_THREADS)
-      reinterpret_cast<int4*>(sub)[i] = int4{0, 0, 0, 0};
-    __syncthreads();
-    int* mysub = sub + (lane & (SEL_SUB - 1));
+  reinterpret_cast<int4*>(cnt)[tid] = int4{0, 0, 0, 0};
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < WIDE_PER; ++i)
-      if (ok[i]) atomicAdd(mysub + (u[i] >> 24) * SEL_SUB, 1);
-    __syncthreads();
-    const int dd = tid >> 2, part = tid & 3;
-    const int4* q4 = reinterpret_cast<const int4*>(sub + dd * SEL_SUB + part * 8);
-    const int4 x = q4[0], y = q4[1];
-    const int c = quad_sum((x.x + x.y) + (x.z + x.w) + (y.x + y.y) + (y.z + y.w));
-    if (part == 0) mine[dd] = (uint16_t)c;
-    return;
+  for (int i = 0; i < WIDE_PER; ++i)
+    if (ok[i]) atomicAdd(&cnt[u[i] >> WIDE_SHIFT], 1);
+  __syncthreads();
+  // bins 4 tid .. 4 tid + 3: their start offsets
+  const int4 c4 = reinterpret_cast<const int4*>(cnt)[tid];
+  int total;
+  const int o0 = block_excl_scan((c4.x + c4.y) + (c4.z + c4.w), wsum, total);
+  const int o1 = o0 + c4.x, o2 = o1 + c4.y, o3 = o2 + c4.z;
+  unsigned char* rec = args.rec + (int64_t)blockIdx.x * WIDE_REC_BYTES;
+  *reinterpret_cast<uint2*>(rec + WREC_OFF + 8 * tid) =
+      make_uint2((uint32_t)o0 | ((uint32_t)o1 << 16), (uint32_t)o2 | ((uint32_t)o3 << 16));
+  if ((tid & (WIDE_GROUP / 4 - 1)) == 0)
+    reinterpret_cast<uint32_t*>(rec + WREC_COARSE)[tid / (WIDE_GROUP / 4)] = (uint32_t)o0;
+  if (tid == 0) {
+    reinterpret_cast<uint16_t*>(rec + WREC_OFF)[WIDE_BINS] = (uint16_t)total;
+    reinterpret_cast<uint32_t*>(rec + WREC_COARSE)[WIDE_GROUPS] = (uint32_t)total;
   }
-  // the first d - 1 picks, then digit d - 1 from the head's chunks
-  int2 st = make_int2(0, w.keep);
-  if (d >= 2) st = w.state[d - 1];
-  if (tid < 256) lhist[tid] = 0;
-  wide_sum<false>(args, w, d - 1, tot, nullptr, red);
-  int dgt, abv;
-  pick_digit(tot, st.y, lane, dgt, abv);
-  const int dshift = 24 - 8 * (d - 1);                   // digit d - 1's lowest bit
-  const uint32_t pmask = d >= 2 ? ~0u << (dshift + 8) : 0u;  // digits before it
-  const uint32_t prefix = (uint32_t)st.x | ((uint32_t)dgt << dshift);
-  if (w.ch == 0 && tid == 0) w.state[d] = make_int2((int)prefix, st.y - abv);
-  // this chunk's keys above the pick (among those matching the earlier
-  // picks), and digit d of its keys that match all d picks
-  const uint32_t pmask_d = ~0u << dshift;
-  int n_above = 0;
+  // the start offsets become the bins' write cursors
+  reinterpret_cast<int4*>(cnt)[tid] = int4{o0, o1, o2, o3};
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < WIDE_PER; ++i) {
-    const bool in_prev = ok[i] && (u[i] & pmask) == (uint32_t)st.x;
-    n_above += __builtin_popcountll(__ballot(in_prev && ((u[i] >> dshift) & 255u) > (uint32_t)dgt));
-    if (ok[i] && (u[i] & pmask_d) == prefix) atomicAdd(&lhist[(u[i] >> (dshift - 8)) & 255u], 1);
+    if (ok[i]) {
+      const int slot = atomicAdd(&cnt[u[i] >> WIDE_SHIFT], 1);
+      spos[slot] = (uint16_t)(wave * WIDE_SEG + i * WAVE + lane);
+    }
   }
-  if (lane == 0) wabove[wave] = n_above;
   __syncthreads();
-  if (tid < 256) mine[tid] = (uint16_t)lhist[tid];
-  if (wave == 0) {
-    const int a = wave_incl_scan(lane < SEL_WAVES ? wabove[lane] : 0);
-    if (lane == SEL_WAVES - 1) reinterpret_cast<int*>(args.above + blockIdx.x)[d - 1] = a;
-  }
+  // positions in bin order, 16 bytes per thread (the slots past the key
+  // count are never read)
+  if (tid < WIDE_CHUNK * 2 / 16)
+    *reinterpret_cast<u32x4*>(rec + WREC_POS + 16 * tid) = reinterpret_cast<const u32x4*>(spos)[tid];
 }
 
 template <bool FUSE>
 __global__ void __launch_bounds__(SEL_THREADS)
-wide_emit_kernel(const WideArgs args) {
-  __shared__ int red[WIDE_SUM_GROUPS][2][256];
-  __shared__ int tot[256];
-  __shared__ int bef[256];
+wide_place_kernel(const WideArgs args) {
+  __shared__ int red[WIDE_SUMS][WIDE_GROUP];
+  __shared__ int acnt[WIDE_GROUP];
+  __shared__ int cs0[WIDE_MAX_CHUNKS];       // each chunk's first bin-B position in its sorted list
+  __shared__ int cabove[WIDE_MAX_CHUNKS];    // its keys in bins above B
+  __shared__ int cstart[WIDE_MAX_CHUNKS];    // its first bin-B key among the head's
+  __shared__ int gtc[WIDE_MAX_CHUNKS];       // its bin-B keys above T
+  __shared__ int eqc[WIDE_MAX_CHUNKS];       // its keys equal to T
+  __shared__ int hist[3][256];
+  __shared__ int wsum[SEL_WAVES];
+  __shared__ uint32_t cval[WIDE_CACHE];
+  __shared__ uint16_t cchk[WIDE_CACHE];
   __shared__ int wtot[2][SEL_WAVES];
   __shared__ int base[2];
   __shared__ int slot_of[FUSE ? WIDE_CHUNK : 1];
@@ -257,31 +236,153 @@ wide_emit_kernel(const WideArgs args) {
 
   uint32_t u[WIDE_PER];
   bool ok[WIDE_PER];
-  wide_load(w, wave, lane, u, ok);
+  wide_load(w, wave, lane, u, ok);  // this chunk's keys, in flight during the search
   uint32_t thr = 0;
   int need_eq = 0;
   const bool all = w.keep == w.N;  // every key is kept, at its own position
   if (!all) {
-    const int2 st = w.state[3];
-    wide_sum<true>(args, w, 3, tot, bef, red);
-    int dgt, abv;
-    pick_digit(tot, st.y, lane, dgt, abv);
-    thr = (uint32_t)st.x | (uint32_t)dgt;
-    need_eq = st.y - abv;
-    // keys above / equal to thr in the head's earlier chunks: their counts
-    // above the first three picks, and their last-digit histograms
-    if (wave == 0) {
-      const int4* ab = args.above + w.item0;
-      int g = 0;
-      for (int c = lane; c < w.ch; c += WAVE) {
-        const int4 a = ab[c];
-        g += a.x + a.y + a.z;
+    const int C = w.nch;
+    const unsigned char* rec0 = args.rec + (int64_t)w.item0 * WIDE_REC_BYTES;
+    auto coarse = [&](int c, int j) {
+      return (int)reinterpret_cast<const uint32_t*>(rec0 + (int64_t)c * WIDE_REC_BYTES + WREC_COARSE)[j];
+    };
+    auto off = [&](int c, int b) {
+      return (int)reinterpret_cast<const uint16_t*>(rec0 + (int64_t)c * WIDE_REC_BYTES + WREC_OFF)[b];
+    };
+    const int j = tid & (WIDE_GROUP - 1), g = tid / WIDE_GROUP;
+
+    // keys of the head at or above bin 64 j (j < 64)
+    {
+      int s = 0;
+      for (int c = g; c < C; c += WIDE_SUMS) s += coarse(c, WIDE_GROUPS) - coarse(c, j);
+      red[g][j] = s;
+    }
+    __syncthreads();
+    if (tid < WIDE_GROUP) {
+      int s = 0;
+#pragma unroll
+      for (int k = 0; k < WIDE_SUMS; ++k) s += red[k][tid];
+      acnt[tid] = s;
+    }
+    __syncthreads();
+    // the last group whose start has keep or more keys at or above it (group
+    // 0 has all N > keep; the counts fall with j, so the lanes that pass are
+    // a prefix)
+    const int gsel = __builtin_popcountll(__ballot(acnt[lane] >= w.keep)) - 1;
+    __syncthreads();
+    // keys at or above bin 64 gsel + 1 + j (bin 4096 reads the key count: none)
+    {
+      const int b = WIDE_GROUP * gsel + 1 + j;
+      int s = 0;
+      for (int c = g; c < C; c += WIDE_SUMS) s += off(c, WIDE_BINS) - off(c, b);
+      red[g][j] = s;
+    }
+    __syncthreads();
+    if (tid < WIDE_GROUP) {
+      int s = 0;
+#pragma unroll
+      for (int k = 0; k < WIDE_SUMS; ++k) s += red[k][tid];
+      acnt[tid] = s;
+    }
+    __syncthreads();
+    // bin B: the last bin with keep or more keys at or above it.  Below 64:
+    // the last bin of the group has fewer than keep (maximality of gsel, or
+    // bin 4096).
+    const int nge = __builtin_popcountll(__ballot(acnt[lane] >= w.keep));
+    const int B = WIDE_GROUP * gsel + nge;
+    const int above = acnt[nge];  // keys in bins above B
+    int krem = w.keep - above;    // keys of bin B to keep (>= 1)
+
+    // every chunk's bin-B range, and its keys above bin B
+    int len = 0;
+    for (int c = tid; c < C; c += SEL_THREADS) {
+      const int s0 = off(c, B), s1 = off(c, B + 1);
+      cs0[c] = s0;
+      cabove[c] = off(c, WIDE_BINS) - s1;
+      gtc[c] = 0;
+      eqc[c] = 0;
+      len = s1 - s0;  // one chunk per thread: C <= WIDE_MAX_CHUNKS = SEL_THREADS
+    }
+    static_assert(WIDE_MAX_CHUNKS == SEL_THREADS, "one chunk per thread in the range scan");
+    int ncand;
+    const int st0 = block_excl_scan(len, wsum, ncand);
+    if (tid < C) cstart[tid] = st0;
+    for (int x = tid; x < 3 * 256; x += SEL_THREADS) (&hist[0][0])[x] = 0;
+    __syncthreads();
+
+    // bin-B key e of the head: its order key and chunk (from LDS once cached)
+    const bool cached = ncand <= WIDE_CACHE;
+    auto fetch = [&](int e, uint32_t& val, int& c) __attribute__((always_inline)) {
+      int lo = 0, hi = C - 1;  // the last chunk whose range starts at or before e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cstart[mid] <= e) lo = mid;
+        else hi = mid - 1;
       }
-      for (int b = dgt + 1 + lane; b < 256; b += WAVE) g += bef[b];
-      g = wave_incl_scan(g);
+      c = lo;
+      const int pos = reinterpret_cast<const uint16_t*>(rec0 + (int64_t)c * WIDE_REC_BYTES + WREC_POS)
+          [cs0[c] + e - cstart[c]];
+      val = sel_key(__float_as_uint(w.sc[c * WIDE_CHUNK + pos]));
+    };
+
+    // three more digits of the threshold over bin B's keys
+    uint32_t P = (uint32_t)B;
+    int sh = WIDE_SHIFT;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int dsh = r == 0 ? 11 : (r == 1 ? 3 : 0);
+      const uint32_t dmask = r < 2 ? 255u : 7u;
+      for (int e = tid; e < ncand; e += SEL_THREADS) {
+        uint32_t val;
+        int c;
+        if (r > 0 && cached) {
+          val = cval[e];
+          c = cchk[e];
+        } else {
+          fetch(e, val, c);
+          if (r == 0 && cached) {
+            cval[e] = val;
+            cchk[e] = (uint16_t)c;
+          }
+        }
+        if ((val >> sh) == P) atomicAdd(&hist[r][(val >> dsh) & dmask], 1);
+      }
+      __syncthreads();
+      int dgt, abv;
+      pick_digit(hist[r], krem, lane, dgt, abv);
+      krem -= abv;
+      P = (P << (sh - dsh)) | (uint32_t)dgt;
+      sh = dsh;
+    }
+    thr = P;
+    need_eq = krem;
+
+    // bin-B keys above / equal to thr, per chunk
+    for (int e = tid; e < ncand; e += SEL_THREADS) {
+      uint32_t val;
+      int c;
+      if (cached) {
+        val = cval[e];
+        c = cchk[e];
+      } else {
+        fetch(e, val, c);
+      }
+      if (val > thr) atomicAdd(&gtc[c], 1);
+      else if (val == thr) atomicAdd(&eqc[c], 1);
+    }
+    __syncthreads();
+    // kept keys above / equal to thr in the head's earlier chunks
+    if (wave == 0) {
+      int gs = 0, es = 0;
+      for (int c = lane; c < w.ch; c += WAVE) {
+        gs += cabove[c] + gtc[c];
+        es += eqc[c];
+      }
+      gs = wave_incl_scan(gs);
+      es = wave_incl_scan(es);
       if (lane == WAVE - 1) {
-        base[0] = g;
-        base[1] = bef[dgt];
+        base[0] = gs;
+        base[1] = es;
       }
     }
     int n_gt = 0, n_eq = 0;

@@ -22,9 +22,8 @@
 #include "select_wide.hpp"
 #include "attention.hpp"
 
-// Scratch of waits_select_compact_noalloc (the wide select's per-chunk digit
-// histograms and counts and per-head picks), one copy per GPU for the life
-// of the process.  In host code `scratch` is a host-side stand-in, not a device
+// Scratch of waits_select_compact_noalloc (the wide select's per-chunk
+// counting-sort records), one copy per GPU for the life of the process.  In host code `scratch` is a host-side stand-in, not a device
 // address: kernels get the address hipGetSymbolAddress reports for their
 // device (device_scratch below).
 constexpr size_t STATIC_SCRATCH_BYTES = WAITS_STATIC_SCRATCH_BYTES;
@@ -754,15 +753,12 @@ void fill_len_table(SeqTable& t, const waits_shape* s, int lo, int hi) {
   }
 }
 
-// Workspace of the several-workgroup select for sequences [lo, hi): per
-// chunk its two 16-bit digit histograms (1 KiB), then per chunk its counts
-// above the first three picks (16 bytes), then per (sequence, head) the
-// four (prefix, keys still to keep) pairs (32 bytes).  0 when every
-// sequence is short enough for one workgroup.
+// Workspace of the several-workgroup select for sequences [lo, hi): one
+// record per chunk (WIDE_REC_BYTES: its bin offsets and its key positions in
+// bin order).  0 when every sequence is short enough for one workgroup.
 struct WideWs {
-  size_t hist_bytes = 0, above_bytes = 0, state_bytes = 0;
   int items = 0;
-  size_t total() const { return hist_bytes + above_bytes + state_bytes; }
+  size_t total() const { return (size_t)items * WIDE_REC_BYTES; }
 };
 WideWs wide_ws(const waits_shape* s, int lo, int hi) {
   WideWs w;
@@ -770,11 +766,9 @@ WideWs wide_ws(const waits_shape* s, int lo, int hi) {
   for (int i = lo; i < hi; ++i) gmax = std::max(gmax, seq_len(s, i));
   if (gmax <= SEL_WIDE_MIN) return w;
   for (int i = lo; i < hi; ++i) w.items += s->n_kv_heads * wide_chunks(seq_len(s, i));
-  w.hist_bytes = (size_t)w.items * WIDE_HIST_BYTES;
-  w.above_bytes = (size_t)w.items * sizeof(int4);
-  w.state_bytes = (size_t)(hi - lo) * s->n_kv_heads * 4 * sizeof(int2);
   return w;
 }
+static_assert(wide_chunks(MAX_SEQ_LEN) <= WIDE_MAX_CHUNKS, "the longest head fits the place kernel's tables");
 
 size_t select_ws_bytes(const waits_shape* s) {
   size_t mx = 0;
@@ -822,14 +816,11 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     int gmax = 0;
     for (int i = lo; i < hi; ++i) gmax = std::max(gmax, seq_len(s, i));
     if (gmax > SEL_WIDE_MIN) {
-      const WideWs w = wide_ws(s, lo, hi);
       WideArgs args;
       std::memset(&args, 0, sizeof(args));
       args.scores = scores;
       args.idx = idx + first_row;
-      args.chist = static_cast<uint16_t*>(ws);
-      args.above = reinterpret_cast<int4*>(static_cast<unsigned char*>(ws) + w.hist_bytes);
-      args.state = reinterpret_cast<int2*>(static_cast<unsigned char*>(ws) + w.hist_bytes + w.above_bytes);
+      args.rec = static_cast<unsigned char*>(ws);
       args.T = s->cu_seqlens[s->batch];
       args.hkv = s->n_kv_heads;
       args.budget = budget;
@@ -848,12 +839,9 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
       }
       args.tab.first[hi - lo] = items;
       if (items > 0) {
-        for (int d = 0; d < 4; ++d) {
-          args.digit = d;
-          hipLaunchKernelGGL(wide_hist_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
-          if (launched() != WAITS_OK) return WAITS_EDEVICE;
-        }
-        hipLaunchKernelGGL((wide_emit_kernel<FUSE>), dim3(items), dim3(SEL_THREADS), 0, stream, args);
+        hipLaunchKernelGGL(wide_sort_kernel, dim3(items), dim3(SEL_THREADS), 0, stream, args);
+        if (launched() != WAITS_OK) return WAITS_EDEVICE;
+        hipLaunchKernelGGL((wide_place_kernel<FUSE>), dim3(items), dim3(SEL_THREADS), 0, stream, args);
         if (launched() != WAITS_OK) return WAITS_EDEVICE;
       }
       continue;
@@ -1146,7 +1134,7 @@ const char* waits_strerror(int code) {
     case WAITS_EWORKSPACE: return "workspace missing or too small";
     case WAITS_EDEVICE: return "HIP runtime refused a kernel launch";
     case WAITS_ESCRATCH:
-      return "batch needs more scratch than the no-allocation call's static 4 MiB (use the workspace call)";
+      return "batch needs more scratch than the no-allocation call's static 16 MiB (use the workspace call)";
     default: return "unknown WAITS status";
   }
 }

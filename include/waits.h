@@ -199,8 +199,11 @@ int waits_select(const waits_shape* shape, const float* scores,
 /*
  * Bytes of device workspace waits_select and waits_select_compact need for
  * this batch: 0 unless a sequence has more than 32768 keys, whose selection
- * is split over several workgroups that meet in the workspace (per-chunk digit
- * histograms and counts, per-head picks).  workspace: device, 16-byte aligned.
+ * is split over workgroups of 4096 keys that meet in the workspace (each
+ * chunk's counting sort by the top 12 bits of its scores: bin offsets and
+ * key positions, 16672 bytes per chunk).  The select writes every word of it
+ * that it reads, so its contents between calls do not matter.
+ * workspace: device, 16-byte aligned.
  */
 int waits_select_workspace_bytes(const waits_shape* shape, int32_t select_budget,
                                  size_t* bytes);
@@ -237,14 +240,14 @@ int waits_select_compact(const waits_shape* shape, const float* scores,
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): no workspace argument, and the same outputs, layouts and
  * error codes as waits_select_compact, bit for bit.  The select of heads of
- * more than 32768 keys needs scratch (per-chunk digit histograms and counts,
- * per-head picks: the bytes waits_select_workspace_bytes reports); this call
- * takes it from a static device array of WAITS_STATIC_SCRATCH_BYTES that the
- * library holds on every GPU it runs on until the process ends, and returns
- * WAITS_ESCRATCH for a batch that needs more: a launch group (32 sequences)
- * with such a head needs 1040 bytes per 4096 keys of each head plus 32 bytes
- * per (sequence, KV head), e.g. 8.5 MiB for 32 sequences x 8 KV heads of
- * 131072 keys.
+ * more than 32768 keys needs scratch (per-chunk counting-sort records: the
+ * bytes waits_select_workspace_bytes reports); this call takes it from a
+ * static device array of WAITS_STATIC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends, and returns WAITS_ESCRATCH
+ * for a batch that needs more: a launch group (32 sequences) with such a
+ * head needs 16672 bytes per 4096 keys (rounded up) of each of its KV heads,
+ * e.g. 4.1 MiB for one sequence of 8 KV heads x 131072 keys; 16 MiB holds
+ * 1006 such chunks.
  * - The scratch of a GPU is the copy on the device `stream` belongs to (the
  *   current device for the null stream); the first call for a device looks
  *   its address up (hipGetSymbolAddress) and keeps it.

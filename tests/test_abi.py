@@ -174,10 +174,11 @@ def test_select_workspace():
     # one workgroup per (sequence, head) up to 32768 keys: no workspace
     assert W.select_workspace_bytes([0, 32768], 8, 128) == 0
     assert W.select_workspace_bytes([0, 0], 8, 128) == 0
-    # longer: 4096-key chunks; per chunk two 256-bin uint16 histograms and an
-    # int4 of counts, then per (sequence, head) four (prefix, keys left) pairs
+    # longer: 4096-key chunks, each with its counting-sort record: 65 coarse
+    # offsets (u32, padded to 272 bytes), 4097 bin offsets (u16, padded to
+    # 4104) and 4096 key positions (u16)
     need = W.select_workspace_bytes([0, 131072, 131072 + 5000], 8, 2048)
-    assert need == 8 * (32 + 2) * (2 * 256 * 2 + 16) + 2 * 8 * 4 * 8
+    assert need == 8 * (32 + 2) * (272 + 2 * 4104 + 2 * 4096)
     s = _shape(cu=[0, 40000], hkv=2)
     lib = W.lib()
     assert lib.waits_select(ctypes.byref(s), FAKE, 64, FAKE, None, 0, None) == W.WAITS_EWORKSPACE
