@@ -8,16 +8,16 @@
 //   wide_sort_kernel    each chunk counting-sorts its keys by the top 12 bits
 //                       of their order key (4096 bins, 1/16 of an octave):
 //                       it writes the bins' start offsets (and every 64th of
-//                       them again, contiguous) and its key positions in bin
-//                       order.  No atomics outside LDS, so the workspace
+//                       them again, contiguous) and its keys' order keys in
+//                       bin order.  No atomics outside LDS, so the workspace
 //                       needs no initial state.
 //   wide_place_kernel   every chunk of a head reads all of the head's chunk
 //                       records: the counts at or above each 64th bin, then
 //                       at or above each bin of the one 64-bin group that
 //                       holds the budget-th largest key, give that key's bin
 //                       B and how many keys lie above it.  The keys of bin B
-//                       (few, as a rule) are read back through the sorted
-//                       positions, and three more radix digits over them
+//                       (few, as a rule) are read back from the sorted
+//                       lists, and three more radix digits over them
 //                       (bits 18-11, 10-3, 2-0) give the threshold T and how
 //                       many keys equal to T are kept.  Each chunk then
 //                       places its own kept keys, slot = (kept keys above T
@@ -29,7 +29,9 @@
 // Every chunk of a head derives the same B and T from the same records.
 // Bin B's keys are held in LDS when they fit (WIDE_CACHE); past that (many
 // equal or nearly equal scores) each pass reads them again from the
-// workspace and the scores, which is slower but gives the same result.
+// workspace, which is slower but gives the same result.  For heads of up to
+// WIDE_FINE_CHUNKS chunks the bin offsets read in the search stay in LDS and
+// give every chunk's bin-B range without another round of loads.
 // Results equal select_kernel's bit for bit (ascending output, -1 / zero
 // rows past the kept count).
 #pragma once
@@ -50,16 +52,18 @@ constexpr int WIDE_GROUPS = WIDE_BINS / WIDE_GROUP;
 constexpr int WIDE_SUMS = SEL_THREADS / WIDE_GROUP;    // chunk groups of the cross-chunk sums
 constexpr int WIDE_MAX_CHUNKS = 1024;                  // chunks of the longest accepted head
 constexpr int WIDE_CACHE = 4096;                       // bin-B keys held in LDS
+constexpr int WIDE_FINE_CHUNKS = 64;                   // chunks whose searched offsets stay in LDS
 // Chunk record: coarse offsets (u32, off[64 j] for j = 0..64), bin offsets
-// (u16, off[b] for b = 0..4096; off[4096] = the chunk's key count), key
-// positions in bin order (u16, relative to the chunk).
+// (u16, off[b] for b = 0..4096; off[4096] = the chunk's key count), order
+// keys in bin order (u32).  A bin-B key only adds to its chunk's counts, so
+// its position is not kept: each chunk places its own keys from the scores.
 constexpr int WREC_COARSE = 0;
 constexpr int WREC_OFF = 272;
-constexpr int WREC_POS = WREC_OFF + 2 * 4104;
-constexpr int WIDE_REC_BYTES = WREC_POS + 2 * WIDE_CHUNK;
+constexpr int WREC_VAL = WREC_OFF + 2 * 4104;
+constexpr int WIDE_REC_BYTES = WREC_VAL + 4 * WIDE_CHUNK;
 static_assert(WREC_OFF >= 4 * (WIDE_GROUPS + 1) && WREC_OFF % 16 == 0, "coarse offsets fit");
-static_assert(WREC_POS % 16 == 0 && WIDE_REC_BYTES % 16 == 0, "16-byte aligned record parts");
-static_assert(WIDE_CHUNK <= 65535, "16-bit offsets and positions");
+static_assert(WREC_VAL % 16 == 0 && WIDE_REC_BYTES % 16 == 0, "16-byte aligned record parts");
+static_assert(WIDE_CHUNK <= 65535, "16-bit offsets");
 static_assert(WIDE_BINS == 4 * SEL_THREADS, "four bins per thread in the chunk's scan");
 
 // Chunks of a key range (an empty one still gets one: its workgroup writes
@@ -147,7 +151,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
 wide_sort_kernel(const WideArgs args) {
   __shared__ __attribute__((aligned(16))) int cnt[WIDE_BINS];
   __shared__ int wsum[SEL_WAVES];
-  __shared__ __attribute__((aligned(16))) uint16_t spos[WIDE_CHUNK];
+  __shared__ __attribute__((aligned(16))) uint32_t sval[WIDE_CHUNK];
   const WideItem w = wide_item(args);
   if (w.keep == w.N) return;  // every key is kept: the place kernel reads no record
   const int tid = threadIdx.x, lane = tid & 63;
@@ -182,14 +186,13 @@ wide_sort_kernel(const WideArgs args) {
   for (int i = 0; i < WIDE_PER; ++i) {
     if (ok[i]) {
       const int slot = atomicAdd(&cnt[u[i] >> WIDE_SHIFT], 1);
-      spos[slot] = (uint16_t)(wave * WIDE_SEG + i * WAVE + lane);
+      sval[slot] = u[i];
     }
   }
   __syncthreads();
-  // positions in bin order, 16 bytes per thread (the slots past the key
+  // order keys in bin order, 16 bytes per thread (the slots past the key
   // count are never read)
-  if (tid < WIDE_CHUNK * 2 / 16)
-    *reinterpret_cast<u32x4*>(rec + WREC_POS + 16 * tid) = reinterpret_cast<const u32x4*>(spos)[tid];
+  *reinterpret_cast<u32x4*>(rec + WREC_VAL + 16 * tid) = reinterpret_cast<const u32x4*>(sval)[tid];
 }
 
 template <bool FUSE>
@@ -197,7 +200,9 @@ __global__ void __launch_bounds__(SEL_THREADS)
 wide_place_kernel(const WideArgs args) {
   __shared__ int red[WIDE_SUMS][WIDE_GROUP];
   __shared__ int acnt[WIDE_GROUP];
-  __shared__ int cs0[WIDE_MAX_CHUNKS];       // each chunk's first bin-B position in its sorted list
+  __shared__ int ctot[WIDE_MAX_CHUNKS];      // each chunk's key count
+  __shared__ int fine[WIDE_FINE_CHUNKS][WIDE_GROUP + 1];  // searched bin offsets (short heads)
+  __shared__ int cs0[WIDE_MAX_CHUNKS];       // each chunk's first bin-B slot in its sorted list
   __shared__ int cabove[WIDE_MAX_CHUNKS];    // its keys in bins above B
   __shared__ int cstart[WIDE_MAX_CHUNKS];    // its first bin-B key among the head's
   __shared__ int gtc[WIDE_MAX_CHUNKS];       // its bin-B keys above T
@@ -254,7 +259,11 @@ wide_place_kernel(const WideArgs args) {
     // keys of the head at or above bin 64 j (j < 64)
     {
       int s = 0;
-      for (int c = g; c < C; c += WIDE_SUMS) s += coarse(c, WIDE_GROUPS) - coarse(c, j);
+      for (int c = g; c < C; c += WIDE_SUMS) {
+        const int tot = coarse(c, WIDE_GROUPS);
+        s += tot - coarse(c, j);
+        if (j == 0) ctot[c] = tot;
+      }
       red[g][j] = s;
     }
     __syncthreads();
@@ -270,11 +279,20 @@ wide_place_kernel(const WideArgs args) {
     // a prefix)
     const int gsel = __builtin_popcountll(__ballot(acnt[lane] >= w.keep)) - 1;
     __syncthreads();
-    // keys at or above bin 64 gsel + 1 + j (bin 4096 reads the key count: none)
+    // keys at or above bin 64 gsel + 1 + j (bin 4096 reads the key count:
+    // none); short heads keep the offsets of bins 64 gsel .. 64 gsel + 64
+    const bool keep_fine = C <= WIDE_FINE_CHUNKS;
     {
       const int b = WIDE_GROUP * gsel + 1 + j;
       int s = 0;
-      for (int c = g; c < C; c += WIDE_SUMS) s += off(c, WIDE_BINS) - off(c, b);
+      for (int c = g; c < C; c += WIDE_SUMS) {
+        const int o = off(c, b);
+        s += ctot[c] - o;
+        if (keep_fine) {
+          fine[c][1 + j] = o;
+          if (j == 0) fine[c][0] = off(c, b - 1);
+        }
+      }
       red[g][j] = s;
     }
     __syncthreads();
@@ -296,9 +314,11 @@ wide_place_kernel(const WideArgs args) {
     // every chunk's bin-B range, and its keys above bin B
     int len = 0;
     for (int c = tid; c < C; c += SEL_THREADS) {
-      const int s0 = off(c, B), s1 = off(c, B + 1);
+      const int bb = B - WIDE_GROUP * gsel;  // 0 .. 63
+      const int s0 = keep_fine ? fine[c][bb] : off(c, B);
+      const int s1 = keep_fine ? fine[c][bb + 1] : off(c, B + 1);
       cs0[c] = s0;
-      cabove[c] = off(c, WIDE_BINS) - s1;
+      cabove[c] = ctot[c] - s1;
       gtc[c] = 0;
       eqc[c] = 0;
       len = s1 - s0;  // one chunk per thread: C <= WIDE_MAX_CHUNKS = SEL_THREADS
@@ -320,9 +340,8 @@ wide_place_kernel(const WideArgs args) {
         else hi = mid - 1;
       }
       c = lo;
-      const int pos = reinterpret_cast<const uint16_t*>(rec0 + (int64_t)c * WIDE_REC_BYTES + WREC_POS)
+      val = reinterpret_cast<const uint32_t*>(rec0 + (int64_t)c * WIDE_REC_BYTES + WREC_VAL)
           [cs0[c] + e - cstart[c]];
-      val = sel_key(__float_as_uint(w.sc[c * WIDE_CHUNK + pos]));
     };
 
     // three more digits of the threshold over bin B's keys

@@ -201,7 +201,7 @@ int waits_select(const waits_shape* shape, const float* scores,
  * this batch: 0 unless a sequence has more than 32768 keys, whose selection
  * is split over workgroups of 4096 keys that meet in the workspace (each
  * chunk's counting sort by the top 12 bits of its scores: bin offsets and
- * key positions, 16672 bytes per chunk).  The select writes every word of it
+ * the scores' order keys, 24864 bytes per chunk).  The select writes every word of it
  * that it reads, so its contents between calls do not matter.
  * workspace: device, 16-byte aligned.
  */
@@ -245,9 +245,9 @@ int waits_select_compact(const waits_shape* shape, const float* scores,
  * static device array of WAITS_STATIC_SCRATCH_BYTES that the library holds
  * on every GPU it runs on until the process ends, and returns WAITS_ESCRATCH
  * for a batch that needs more: a launch group (32 sequences) with such a
- * head needs 16672 bytes per 4096 keys (rounded up) of each of its KV heads,
- * e.g. 4.1 MiB for one sequence of 8 KV heads x 131072 keys; 16 MiB holds
- * 1006 such chunks.
+ * head needs 24864 bytes per 4096 keys (rounded up) of each of its KV heads,
+ * e.g. 6.1 MiB for one sequence of 8 KV heads x 131072 keys; 16 MiB holds
+ * 674 such chunks.
  * - The scratch of a GPU is the copy on the device `stream` belongs to (the
  *   current device for the null stream); the first call for a device looks
  *   its address up (hipGetSymbolAddress) and keeps it.

@@ -176,9 +176,9 @@ def test_select_workspace():
     assert W.select_workspace_bytes([0, 0], 8, 128) == 0
     # longer: 4096-key chunks, each with its counting-sort record: 65 coarse
     # offsets (u32, padded to 272 bytes), 4097 bin offsets (u16, padded to
-    # 4104) and 4096 key positions (u16)
+    # 4104) and 4096 order keys (u32)
     need = W.select_workspace_bytes([0, 131072, 131072 + 5000], 8, 2048)
-    assert need == 8 * (32 + 2) * (272 + 2 * 4104 + 2 * 4096)
+    assert need == 8 * (32 + 2) * (272 + 2 * 4104 + 4 * 4096)
     s = _shape(cu=[0, 40000], hkv=2)
     lib = W.lib()
     assert lib.waits_select(ctypes.byref(s), FAKE, 64, FAKE, None, 0, None) == W.WAITS_EWORKSPACE
