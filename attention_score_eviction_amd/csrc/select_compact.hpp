@@ -33,9 +33,10 @@
 // scan, no atomics.
 //
 // FUSE: the same workgroup then gathers the kept K and V rows (bit copies,
-// 16-byte vectors; zero rows past the kept count), so select and compact are
-// one launch.  Once P is known (after pass 3), each lane requests into L2 the
-// K and V rows of one of its keys at or above P (kept, or still undecided):
+// 16-byte vectors, four per thread in flight; zero rows past the kept
+// count), so select and compact are one launch.  Once P is known (after
+// pass 3), each lane requests into L2 the K and V rows of one of its keys
+// at or above P (kept, or still undecided):
 // plain loads whose values are consumed only after the gather, so pass 4,
 // the counts and the output run while they are in flight and the gather
 // finds most rows in L2.  A lane with several such keys (rare: about one key
@@ -62,6 +63,42 @@ __device__ __forceinline__ uint32_t sel_key(uint32_t u) { return (int32_t)u < 0 
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Row copies of the gather: 16-byte vectors x in [x0, total) stepping by
+// `stride`, U per trip with every load issued before the first store (a
+// workgroup that keeps many rows would otherwise wait one memory round trip
+// per vector).  src(x), dst(x): byte offsets of vector x in K and V and in
+// the outputs; src(x) < 0 writes a zero vector.
+template <int U, typename SrcF, typename DstF>
+__device__ __forceinline__ void gather_vectors(const unsigned char* k, const unsigned char* v,
+                                               unsigned char* k_out, unsigned char* v_out, int x0,
+                                               int total, int stride, SrcF src, DstF dst) {
+  for (int xb = x0; xb < total; xb += U * stride) {
+    u32x4 kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = xb + u * stride;
+      kv[u] = u32x4{0u, 0u, 0u, 0u};
+      vv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (x < total) {
+        const int64_t sx = src(x);
+        if (sx >= 0) {
+          kv[u] = ld16(k + sx);
+          vv[u] = ld16(v + sx);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = xb + u * stride;
+      if (x < total) {
+        const int64_t dx = dst(x);
+        st16(k_out + dx, kv[u]);
+        st16(v_out + dx, vv[u]);
+      }
+    }
+  }
 }
 
 // Wave-uniform pick from a 256-bin histogram: the digit d whose keys hold the
@@ -259,17 +296,11 @@ select_kernel(const SelectArgs args) {
     __syncthreads();
     const int total = budget << vs;
     const int64_t obase = ((int64_t)p * args.hkv + h) * budget * rb;
-    for (int x = tid; x < total; x += SEL_THREADS) {
-      const int j = x >> vs, c = x & ((1 << vs) - 1);
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (j < keep) {
-        const int64_t src = kbase + (int64_t)sel[j] * kv_row + c * 16;
-        kv = ld16(args.k + src);
-        vv = ld16(args.v + src);
-      }
-      st16(args.k_out + obase + (int64_t)j * rb + c * 16, kv);
-      st16(args.v_out + obase + (int64_t)j * rb + c * 16, vv);
-    }
+    const int cm = (1 << vs) - 1;
+    gather_vectors<4>(
+        args.k, args.v, args.k_out, args.v_out, tid, total, SEL_THREADS,
+        [&](int x) { return (x >> vs) < keep ? kbase + (int64_t)sel[x >> vs] * kv_row + (x & cm) * 16 : (int64_t)-1; },
+        [&](int x) { return obase + (int64_t)(x >> vs) * rb + (x & cm) * 16; });
     // keeps the L2 requests alive; budget >= 1, so nothing is written
     if (budget < 0) out[tid] = (int32_t)(pfv[0] ^ pfv[1] ^ pfv[2] ^ pfv[3]);
   }

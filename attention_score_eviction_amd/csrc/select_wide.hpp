@@ -450,13 +450,14 @@ wide_place_kernel(const WideArgs args) {
   if constexpr (FUSE) {
     __syncthreads();
     const int total = nkept << vs;
-    for (int x = tid; x < total; x += SEL_THREADS) {
-      const int j = x >> vs, c = x & ((1 << vs) - 1);
-      const int64_t src = kbase + (int64_t)pos_of[j] * args.st.kv_tok * args.elt + c * 16;
-      const int64_t dst = obase + (int64_t)slot_of[j] * rb + c * 16;
-      st16(args.k_out + dst, ld16(args.k + src));
-      st16(args.v_out + dst, ld16(args.v + src));
-    }
+    // eight vectors per thread in flight: the kept keys can crowd into a few
+    // chunks (at a = 0 the first keys hold the largest scores)
+    const int cm = (1 << vs) - 1;
+    const int64_t kv_row = args.st.kv_tok * args.elt;
+    gather_vectors<8>(
+        args.k, args.v, args.k_out, args.v_out, tid, total, SEL_THREADS,
+        [&](int x) { return kbase + (int64_t)pos_of[x >> vs] * kv_row + (x & cm) * 16; },
+        [&](int x) { return obase + (int64_t)slot_of[x >> vs] * rb + (x & cm) * 16; });
   }
 }
 
