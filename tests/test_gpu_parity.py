@@ -643,6 +643,33 @@ def test_select_threshold_zero(n):
         assert torch.equal(vc[0, h].view(torch.int16), v[rows, h].view(torch.int16))
 
 
+@pytest.mark.parametrize("n,budget", [(300000, 2048), (70000, 4000)])
+def test_wide_select_long_heads_and_crowded_chunks(n, budget):
+    # heads past 64 chunks of 4096 keys (300000 keys: the bin offsets are read
+    # again rather than held in LDS), and scores falling with position as at
+    # a = 0, so the first chunk keeps almost every kept row (4000 of its
+    # 4096: the fused gather runs several trips in one workgroup); kept
+    # positions against the oracle's top-k, rows bit for bit
+    _say(f"wide select n={n} budget={budget}")
+    rng = np.random.default_rng(3000 + n)
+    s = np.empty((2, n), dtype=np.float32)
+    s[0] = (rng.random(n) ** 3).astype(np.float32)
+    s[1] = (1.0 / (1.0 + np.arange(n) / 8.0)).astype(np.float32) * np.float32(1 + 0.01 * rng.random())
+    s[1, rng.integers(0, n, n // 100)] *= np.float32(3.0)
+    sd = torch.from_numpy(s).to(DEV)
+    k = torch.randn((n, 2, 64), device=DEV).to(torch.bfloat16)
+    v = torch.randn((n, 2, 64), device=DEV).to(torch.bfloat16)
+    idx, kc, vc = W.select_compact(sd, k, v, [0, n], budget)
+    got = idx.cpu().numpy()
+    for h in range(2):
+        np.testing.assert_array_equal(got[0, h], orc.select_topk(s[h].astype(np.float64), budget))
+        rows = torch.from_numpy(got[0, h].astype(np.int64)).to(DEV)
+        assert torch.equal(kc[0, h].view(torch.int16), k[rows, h].view(torch.int16))
+        assert torch.equal(vc[0, h].view(torch.int16), v[rows, h].view(torch.int16))
+    if n == 70000:
+        assert int((got[0, 1] < 4096).sum()) > 3500   # the first chunk keeps most rows
+
+
 @pytest.mark.parametrize("lengths,budget", [([3000, 17000, 40, 0, 33000], 256), ([5000, 9000], 10000),
                                             ([700] * 40, 64), ([128, 127, 129], 128)])
 def test_select_compact_fused_matches_separate(lengths, budget):
