@@ -133,9 +133,10 @@ int run_mode(int threads, int blocks, int iters, float* out, long long* stamps, 
 // TM_MFMA and TM_EPI run only one of the two streams.
 enum TileMode { TM_MFMA = 0, TM_EPI = 1, TM_MIX = 2 };
 
-template <int TM, int G, int PRIO>
-__global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps, int iters, float c) {
+template <int TM, int G, int PRIO, int NT = 4, int LB = 512>
+__global__ void __launch_bounds__(LB) tile_kernel(float* out, long long* stamps, int iters, float c) {
   static_assert(G >= 1 && G <= 32 && 32 % G == 0, "G divides 32");
+  static_assert(NT >= 1 && NT <= 4 && (NT == 4 || (TM == TM_MIX && G == 32)), "fewer tiles: one cluster only");
   const int tid = threadIdx.x;
   bf16x8 a[4], b[2][4];
   for (int s = 0; s < 4; ++s)
@@ -144,9 +145,9 @@ __global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps
       b[0][s][i] = (__bf16)(0.002f * (tid - i + s));
       b[1][s][i] = (__bf16)(0.003f * (tid - i - s));
     }
-  f32x4 acc[2][8];
+  f32x4 acc[2][2 * NT];
   for (int p = 0; p < 2; ++p)
-    for (int m = 0; m < 8; ++m) acc[p][m] = f32x4{0.01f * m, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 2 * NT; ++m) acc[p][m] = f32x4{0.01f * m, 0.f, 0.f, 0.f};
   float m4[4] = {0.1f, 0.2f, 0.3f, 0.4f}, sum[4] = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   const long long t0 = __builtin_amdgcn_s_memtime();
@@ -165,7 +166,7 @@ __global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
               const int m = t * 2 + kt;
@@ -175,11 +176,11 @@ __global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
       } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) asm volatile("" : "+v"(acc[par ^ 1][m]));
+        for (int m = 0; m < 2 * NT; ++m) asm volatile("" : "+v"(acc[par ^ 1][m]));
       }
       if constexpr (TM != TM_MFMA) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NT; ++t) {
           float sv = 0.f;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps
   const long long r1 = __builtin_amdgcn_s_memrealtime();
   float r = 0.f;
   for (int p = 0; p < 2; ++p)
-    for (int m = 0; m < 8; ++m) r += acc[p][m][0] + acc[p][m][3];
+    for (int m = 0; m < 2 * NT; ++m) r += acc[p][m][0] + acc[p][m][3];
   for (int t = 0; t < 4; ++t) r += sum[t];
   out[blockIdx.x * blockDim.x + tid] = r;
   if ((tid & 63) == 0) {
@@ -222,10 +223,12 @@ __global__ void __launch_bounds__(512) tile_kernel(float* out, long long* stamps
 
 // res[0] = cycles per iteration (32 MFMAs and/or 32 epilogue elements per
 // wave) of the slowest wave, res[1] = shader clock in GHz.
-template <int TM, int G, int PRIO>
+template <int TM, int G, int PRIO, int NT = 4, int LB = 512>
 int run_tile(int threads, int blocks, int iters, float* out, long long* stamps, double* res) {
-  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO>), dim3(blocks), dim3(threads), 0, 0, out, stamps, 16, 1.0001f);
-  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO>), dim3(blocks), dim3(threads), 0, 0, out, stamps, iters, 1.0001f);
+  if (threads > LB) return 1;
+  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO, NT, LB>), dim3(blocks), dim3(threads), 0, 0, out, stamps, 16, 1.0001f);
+  hipLaunchKernelGGL((tile_kernel<TM, G, PRIO, NT, LB>), dim3(blocks), dim3(threads), 0, 0, out, stamps, iters,
+                     1.0001f);
   if (hipDeviceSynchronize() != hipSuccess) return 4;
   const int waves = blocks * (threads / 64);
   std::vector<long long> h((size_t)waves * 2);
@@ -302,6 +305,27 @@ int waits_ubench_tile(int threads, int blocks, int iters, double* res) {
   rc = rc ? rc : run_tile<TM_MIX, 4, 0>(threads, blocks, iters, out, stamps, res + 12);
   rc = rc ? rc : run_tile<TM_MIX, 2, 0>(threads, blocks, iters, out, stamps, res + 14);
   rc = rc ? rc : run_tile<TM_MIX, 1, 0>(threads, blocks, iters, out, stamps, res + 16);
+  (void)hipFree(out);
+  (void)hipFree(stamps);
+  return rc;
+}
+
+// The kernels' one-cluster order at more waves per SIMD: configurations
+// (threads, row tiles per wave) = (512, 4), (768, 4), (768, 3), (1024, 3),
+// (1024, 2) on `blocks` workgroups; res[2 * i + {0, 1}] = cycles per
+// iteration of the slowest wave and the clock in GHz.
+int waits_ubench_tile_waves(int blocks, int iters, double* res) {
+  if (iters < 2 || iters % 2) return 1;
+  float* out = nullptr;
+  long long* stamps = nullptr;
+  if (hipMalloc(&out, sizeof(float) * blocks * 1024) != hipSuccess) return 4;
+  if (hipMalloc(&stamps, sizeof(long long) * 2 * blocks * 16) != hipSuccess) return 4;
+  int rc = 0;
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1, 4, 512>(512, blocks, iters, out, stamps, res + 0);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1, 4, 768>(768, blocks, iters, out, stamps, res + 2);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1, 3, 768>(768, blocks, iters, out, stamps, res + 4);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1, 3, 1024>(1024, blocks, iters, out, stamps, res + 6);
+  rc = rc ? rc : run_tile<TM_MIX, 32, 1, 2, 1024>(1024, blocks, iters, out, stamps, res + 8);
   (void)hipFree(out);
   (void)hipFree(stamps);
   return rc;

@@ -616,6 +616,7 @@ UBENCH_MODES = ["mfma: 8 MFMA 16x16x32 bf16", "triple: 8 (fma, exp, add)", "exp:
                 "clusters: 8 MFMA then 8 triples", "clusters, MFMA at raised wave priority",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 triples",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 fma", "split: waves 0-3 8 MFMA, waves 4-7 8 exp"]
+UBENCH_WAVES = [(512, 4), (768, 4), (768, 3), (1024, 3), (1024, 2)]  # (threads, row tiles per wave)
 UBENCH_TILE = ["MFMAs only", "epilogue only", "one cluster, MFMAs at raised priority",
                "groups of 32 MFMAs", "groups of 16", "groups of 8", "groups of 4", "groups of 2",
                "groups of 1"]
@@ -653,6 +654,17 @@ def ubench(args):
                           "cycles_per_iteration": {m: {"slowest_wave": round(res[2 * i], 1),
                                                        "clock_ghz": round(res[2 * i + 1], 3)}
                                                    for i, m in enumerate(UBENCH_TILE)}}), flush=True)
+    # the kernels' one-cluster order at two to four waves per SIMD
+    res = (ctypes.c_double * (2 * len(UBENCH_WAVES)))()
+    rc = lib.waits_ubench_tile_waves(256, 4000, res)
+    if rc:
+        raise SystemExit(f"waits_ubench_tile_waves failed ({rc})")
+    print(json.dumps({"ubench": "pass shape, one cluster at raised priority, by waves per SIMD",
+                      "workgroups": 256,
+                      "simd_cycles_per_mfma": {f"{t} threads ({t // 256} waves/SIMD), {nt} row tiles": {
+                          "cycles": round(res[2 * i] / (t // 256 * 8 * nt), 2),
+                          "clock_ghz": round(res[2 * i + 1], 3)}
+                          for i, (t, nt) in enumerate(UBENCH_WAVES)}}), flush=True)
 
 
 def main():
