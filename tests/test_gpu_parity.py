@@ -670,6 +670,41 @@ def test_wide_select_long_heads_and_crowded_chunks(n, budget):
         assert int((got[0, 1] < 4096).sum()) > 3500   # the first chunk keeps most rows
 
 
+def test_wide_select_ignores_workspace_contents():
+    # the several-workgroup select reads only workspace words it wrote in the
+    # same call: a workspace full of 0xff bytes, or one left by a call on
+    # other inputs, gives the same kept positions and rows bit for bit
+    _say("wide select, workspace contents")
+    rng = np.random.default_rng(77)
+    lengths = [40000, 131072, 0, 33000]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(cu[-1])
+    s = (rng.random((2, T)) ** 5).astype(np.float32)
+    s[:, rng.integers(0, T, T // 7)] = np.float32(0.5)
+    sd = torch.from_numpy(s).to(DEV)
+    k = torch.randn((T, 2, 64), device=DEV).to(torch.bfloat16)
+    v = torch.randn((T, 2, 64), device=DEV).to(torch.bfloat16)
+    budget = 1500
+    nbytes = W.waits.select_workspace_bytes(cu, 2, budget)
+    assert nbytes > 0
+    want = W.select_compact(sd, k, v, cu, budget, workspace=torch.zeros(nbytes, dtype=torch.uint8, device=DEV))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    got1 = W.select_compact(sd, k, v, cu, budget, workspace=ws)
+    other = torch.from_numpy((rng.random((2, T)) ** 2).astype(np.float32)).to(DEV)
+    W.select_compact(other, k, v, cu, budget, workspace=ws)          # leaves its own records behind
+    got2 = W.select_compact(sd, k, v, cu, budget, workspace=ws)
+    torch.cuda.synchronize()
+    for got in (got1, got2):
+        assert torch.equal(got[0], want[0])
+        assert torch.equal(got[1].view(torch.int16), want[1].view(torch.int16))
+        assert torch.equal(got[2].view(torch.int16), want[2].view(torch.int16))
+    for p_ in range(len(lengths)):
+        lo, hi = int(cu[p_]), int(cu[p_ + 1])
+        for h in range(2):
+            np.testing.assert_array_equal(want[0][p_, h].cpu().numpy(),
+                                          orc.select_topk(s[h, lo:hi].astype(np.float64), budget))
+
+
 @pytest.mark.parametrize("lengths,budget", [([3000, 17000, 40, 0, 33000], 256), ([5000, 9000], 10000),
                                             ([700] * 40, 64), ([128, 127, 129], 128)])
 def test_select_compact_fused_matches_separate(lengths, budget):
