@@ -862,7 +862,12 @@ int run_select(const waits_shape* s, const float* scores, int32_t budget, int32_
     fill_len_table(args.tab, s, lo, hi);
     const dim3 grid((hi - lo) * s->n_kv_heads);
     static_assert(SEL_WIDE_MIN == SEL_THREADS * 32, "one workgroup holds at most 32 keys per lane");
-    if (gmax <= SEL_THREADS * 16)
+    // slots per lane: the fewest that hold the launch group's longest head
+    if (gmax <= SEL_THREADS * 4)
+      hipLaunchKernelGGL((select_kernel<4, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+    else if (gmax <= SEL_THREADS * 8)
+      hipLaunchKernelGGL((select_kernel<8, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
+    else if (gmax <= SEL_THREADS * 16)
       hipLaunchKernelGGL((select_kernel<16, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);
     else
       hipLaunchKernelGGL((select_kernel<32, FUSE>), grid, dim3(SEL_THREADS), 0, stream, args);

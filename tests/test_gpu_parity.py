@@ -603,9 +603,10 @@ def test_select_on_arbitrary_scores(n, budget):
         np.testing.assert_array_equal(idx[0, h], orc.select_topk(s[h].astype(np.float64), budget))
 
 
-@pytest.mark.parametrize("n", [1, 63, 64, 1023, 1024, 1025, 16384, 16385, 32768, 32769, 65600])
+@pytest.mark.parametrize("n", [1, 63, 64, 1023, 1024, 1025, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 65600])
 def test_select_segment_boundaries(n):
     # key counts around the per-wave segment sizes and the register-cache limits
+    # (4, 8, 16 and 32 slots per lane up to 4096, 8192, 16384 and 32768 keys)
     _say(f"select boundaries n={n}")
     rng = np.random.default_rng(1000 + n)
     s = (rng.random((2, n)) ** 6).astype(np.float32)
