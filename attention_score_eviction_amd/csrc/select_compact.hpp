@@ -51,6 +51,12 @@
 
 namespace waits {
 
+// Phase marks for the microbenchmark library, which defines WAITS_SELECT_MARK
+// to record a timestamp per phase; empty in the WAITS library.
+#ifndef WAITS_SELECT_MARK
+#define WAITS_SELECT_MARK(k)
+#endif
+
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 constexpr int SEL_SUB = 32;          // sub-counters per digit
@@ -155,6 +161,7 @@ select_kernel(const SelectArgs args) {
   const int64_t kv_row = args.st.kv_tok * args.elt;
 
   uint32_t pfv[4] = {0u, 0u, 0u, 0u};  // L2 requests (values unused)
+  WAITS_SELECT_MARK(0);
 
   if (keep == N) {  // every key is kept
     for (int j = tid; j < N; j += SEL_THREADS) {
@@ -176,6 +183,7 @@ select_kernel(const SelectArgs args) {
     hist[tid >> 8][tid & 255] = 0;
     static_assert(SEL_THREADS == 4 * 256, "one histogram word per thread");
     __syncthreads();
+    WAITS_SELECT_MARK(1);
 
     // pass 1: top byte
     {
@@ -189,6 +197,7 @@ select_kernel(const SelectArgs args) {
       const int c = quad_sum((x.x + x.y) + (x.z + x.w) + (y.x + y.y) + (y.z + y.w));
       if (part == 0) hist[0][d] = c;
       __syncthreads();
+      WAITS_SELECT_MARK(2);
     }
     int dgt, above;
     pick_digit(hist[0], keep, lane, dgt, above);
@@ -202,6 +211,7 @@ select_kernel(const SelectArgs args) {
       atomicAdd(a, 1);
     }
     __syncthreads();
+    WAITS_SELECT_MARK(3);
     pick_digit(hist[1], krem, lane, dgt, above);
     krem -= above;
     const uint32_t P16 = (d1 << 8) | (uint32_t)dgt;
@@ -235,6 +245,7 @@ select_kernel(const SelectArgs args) {
       }
     }
     __syncthreads();
+    WAITS_SELECT_MARK(4);
     pick_digit(hist[2], krem, lane, dgt, above);
     krem -= above;
     const uint32_t P24 = (P16 << 8) | (uint32_t)dgt;
@@ -248,6 +259,7 @@ select_kernel(const SelectArgs args) {
       }
     }
     __syncthreads();
+    WAITS_SELECT_MARK(5);
     pick_digit(hist[3], krem, lane, dgt, above);
     krem -= above;
     const uint32_t thr = (P24 << 8) | (uint32_t)dgt;
@@ -269,6 +281,7 @@ select_kernel(const SelectArgs args) {
       wtot[1][wave] = n_eq;
     }
     __syncthreads();
+    WAITS_SELECT_MARK(6);
     // keys above / equal to thr in earlier waves
     int gb = wave_incl_scan(lane < wave ? wtot[0][lane] : 0);
     int eb = wave_incl_scan(lane < wave ? wtot[1][lane] : 0);
@@ -292,6 +305,7 @@ select_kernel(const SelectArgs args) {
     }
   }
 
+  WAITS_SELECT_MARK(7);
   if constexpr (FUSE) {
     __syncthreads();
     const int total = budget << vs;
@@ -303,6 +317,7 @@ select_kernel(const SelectArgs args) {
         [&](int x) { return obase + (int64_t)(x >> vs) * rb + (x & cm) * 16; });
     // keeps the L2 requests alive; budget >= 1, so nothing is written
     if (budget < 0) out[tid] = (int32_t)(pfv[0] ^ pfv[1] ^ pfv[2] ^ pfv[3]);
+    WAITS_SELECT_MARK(8);
   }
 }
 

@@ -14,7 +14,17 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <vector>
+
+// The WAITS select kernel with its phase marks recorded: thread 0 of each
+// workgroup stamps the shader clock (s_memtime) at the end of each phase.
+__device__ long long g_select_marks[256 * 9];
+#define WAITS_SELECT_MARK(k)                                                                 \
+  do {                                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < 256) g_select_marks[blockIdx.x * 9 + (k)] = __builtin_amdgcn_s_memtime(); \
+  } while (0)
+#include "select_compact.hpp"
 
 namespace {
 
@@ -283,6 +293,99 @@ int waits_ubench_mix(int threads, int blocks, int iters, double* res, int* simd)
 }
 
 int waits_ubench_modes(void) { return N_MODES; }
+
+// The fused select+compact (select_kernel<16, true>) on `layers` sequences of
+// n keys, 8 KV heads, head_dim 128 (bf16), budget kept keys per head: the
+// headline's shape at layers = 32, n = 16384, budget = 128.  Scores: a fixed
+// hash of the position, most in [0, 1e-3) and one key in a hundred near 1 (a
+// heavy-hitter-like tail).  res[0..7] = median cycles per workgroup of the
+// phases between marks k and k + 1 (0 start, 1 first barrier, 2..5 the four
+// radix passes, 6 totals, 7 output placed, 8 gather done), res[8] = median
+// total cycles, res[9] = microseconds per launch (HIP events over 20).
+int waits_ubench_select(int layers, int n, int budget, double* res) {
+  const int hkv = 8, d = 128, heads = layers * hkv;
+  if (layers < 1 || layers > waits::MAXB || heads > 256 || n < 1 || n > 16 * waits::SEL_THREADS) return 1;
+  if (budget < 1 || budget > waits::SEL_FUSE_MAX) return 1;
+  const int64_t T = (int64_t)layers * n;
+  std::vector<float> hs((size_t)hkv * T);
+  for (size_t i = 0; i < hs.size(); ++i) {
+    uint32_t x = (uint32_t)i * 2654435761u;
+    x ^= x >> 15;
+    x *= 2246822519u;
+    x ^= x >> 13;
+    const float f = (float)(x >> 8) * (1.0f / 16777216.0f);
+    hs[i] = (x % 100u == 0u) ? 0.5f + 0.5f * f : 1e-3f * f * f;
+  }
+  float* sc = nullptr;
+  unsigned char *k = nullptr, *v = nullptr, *ko = nullptr, *vo = nullptr;
+  int32_t* idx = nullptr;
+  const size_t kv_bytes = (size_t)T * hkv * d * 2, out_bytes = (size_t)heads * budget * d * 2;
+  int rc = 0;
+  if (hipMalloc(&sc, hs.size() * 4) != hipSuccess || hipMalloc(&k, kv_bytes) != hipSuccess ||
+      hipMalloc(&v, kv_bytes) != hipSuccess || hipMalloc(&ko, out_bytes) != hipSuccess ||
+      hipMalloc(&vo, out_bytes) != hipSuccess || hipMalloc(&idx, (size_t)heads * budget * 4) != hipSuccess)
+    rc = 4;
+  if (!rc && hipMemcpy(sc, hs.data(), hs.size() * 4, hipMemcpyHostToDevice) != hipSuccess) rc = 4;
+  if (!rc && (hipMemset(k, 0x3c, kv_bytes) != hipSuccess || hipMemset(v, 0x3d, kv_bytes) != hipSuccess)) rc = 4;
+  std::vector<long long> marks(256 * 9);
+  if (!rc) {
+    waits::SelectArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.scores = sc;
+    a.idx = idx;
+    a.T = T;
+    a.hkv = hkv;
+    a.budget = budget;
+    a.k = k;
+    a.v = v;
+    a.k_out = ko;
+    a.v_out = vo;
+    a.st.kv_tok = (int64_t)hkv * d;
+    a.st.kv_head = d;
+    a.elt = 2;
+    a.row_shift = 4;  // 256-byte rows: 16 vectors of 16 bytes
+    a.tab.nb = layers;
+    for (int i = 0; i < layers; ++i) {
+      a.tab.n[i] = n;
+      a.tab.tok0[i] = (int64_t)i * n;
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) rc = 4;
+    for (int w = 0; w < 5 && !rc; ++w)
+      hipLaunchKernelGGL((waits::select_kernel<16, true>), dim3(heads), dim3(waits::SEL_THREADS), 0, 0, a);
+    if (!rc && hipDeviceSynchronize() != hipSuccess) rc = 4;
+    if (!rc && hipMemcpyFromSymbol(marks.data(), HIP_SYMBOL(g_select_marks), sizeof(long long) * marks.size()) !=
+                   hipSuccess)
+      rc = 4;
+    if (!rc) {
+      (void)hipEventRecord(e0, 0);
+      for (int w = 0; w < 20; ++w)
+        hipLaunchKernelGGL((waits::select_kernel<16, true>), dim3(heads), dim3(waits::SEL_THREADS), 0, 0, a);
+      (void)hipEventRecord(e1, 0);
+      float ms = 0.f;
+      if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) rc = 4;
+      res[9] = ms * 1e3 / 20.0;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+  }
+  if (!rc) {
+    std::vector<long long> ph((size_t)heads);
+    for (int k2 = 0; k2 <= 8; ++k2) {
+      for (int h = 0; h < heads; ++h)
+        ph[h] = k2 < 8 ? marks[h * 9 + k2 + 1] - marks[h * 9 + k2] : marks[h * 9 + 8] - marks[h * 9];
+      std::nth_element(ph.begin(), ph.begin() + heads / 2, ph.end());
+      res[k2] = (double)ph[heads / 2];
+    }
+  }
+  (void)hipFree(sc);
+  (void)hipFree(k);
+  (void)hipFree(v);
+  (void)hipFree(ko);
+  (void)hipFree(vo);
+  (void)hipFree(idx);
+  return rc;
+}
 
 // The passes' shape (tile_kernel) on `blocks` workgroups of `threads` (256
 // or 512) threads; configurations in order: MFMAs only, epilogue only, one

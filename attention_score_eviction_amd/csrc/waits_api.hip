@@ -754,7 +754,7 @@ void fill_len_table(SeqTable& t, const waits_shape* s, int lo, int hi) {
 }
 
 // Workspace of the several-workgroup select for sequences [lo, hi): one
-// record per chunk (WIDE_REC_BYTES: its bin offsets and its key positions in
+// record per chunk (WIDE_REC_BYTES: its bin offsets and its order keys in
 // bin order).  0 when every sequence is short enough for one workgroup.
 struct WideWs {
   int items = 0;

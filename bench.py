@@ -617,6 +617,9 @@ UBENCH_MODES = ["mfma: 8 MFMA 16x16x32 bf16", "triple: 8 (fma, exp, add)", "exp:
                 "split: waves 0-3 8 MFMA, waves 4-7 8 triples",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 fma", "split: waves 0-3 8 MFMA, waves 4-7 8 exp"]
 UBENCH_WAVES = [(512, 4), (768, 4), (768, 3), (1024, 3), (1024, 2)]  # (threads, row tiles per wave)
+UBENCH_SELECT = ["start to first barrier (loads issued, LDS cleared)", "pass 1 (top byte, waits for the scores)",
+                 "pass 2", "pass 3 (and the L2 requests)", "pass 4", "totals", "output placed", "gather",
+                 "total"]
 UBENCH_TILE = ["MFMAs only", "epilogue only", "one cluster, MFMAs at raised priority",
                "groups of 32 MFMAs", "groups of 16", "groups of 8", "groups of 4", "groups of 2",
                "groups of 1"]
@@ -654,6 +657,15 @@ def ubench(args):
                           "cycles_per_iteration": {m: {"slowest_wave": round(res[2 * i], 1),
                                                        "clock_ghz": round(res[2 * i + 1], 3)}
                                                    for i, m in enumerate(UBENCH_TILE)}}), flush=True)
+    # the headline's select+compact with its phases stamped
+    res = (ctypes.c_double * 10)()
+    rc = lib.waits_ubench_select(32, 16384, 128, res)
+    if rc:
+        raise SystemExit(f"waits_ubench_select failed ({rc})")
+    print(json.dumps({"ubench": "select_kernel<16, true> phases (32 sequences x 8 KV heads x 16384 keys, "
+                                "budget 128, head_dim 128)",
+                      "median_cycles_per_workgroup": {nm: round(res[i], 0) for i, nm in enumerate(UBENCH_SELECT)},
+                      "us_per_launch": round(res[9], 2)}), flush=True)
     # the kernels' one-cluster order at two to four waves per SIMD
     res = (ctypes.c_double * (2 * len(UBENCH_WAVES)))()
     rc = lib.waits_ubench_tile_waves(256, 4000, res)
