@@ -5,6 +5,12 @@ tensors into pointers, strides and the caller's current HIP stream, and
 raises ``WaitsError`` on a nonzero status.  There is no fallback: if the
 library is not built, every call raises.
 
+Calls that take a ``workspace`` allocate one of the size the matching
+``*_workspace_bytes`` query returns when none is given; a caller's workspace
+is passed as it is, and the library rejects one that is too small
+(``WaitsError`` with status WAITS_EWORKSPACE), so a call with its workspace
+makes no separate size query.
+
 Layouts (token-major packed batch, positions restart per sequence):
   q [T, Hq, d], k / v [T, Hkv, d]  (any strides with d contiguous)
   lse [Hq, T] fp32, scores [Hkv, T] fp32
@@ -173,8 +179,8 @@ class _Marshal:
         self.shape.pass2 = _PASS2[pass2]
         self.a = self.b = None
         if a is not None:
-            self.a = np.ascontiguousarray(np.broadcast_to(np.asarray(a, np.float32), (batch,)))
-            self.b = np.ascontiguousarray(np.broadcast_to(np.asarray(b, np.int32), (batch,)))
+            self.a = _per_seq(a, np.float32, batch)
+            self.b = _per_seq(b, np.int32, batch)
 
     @property
     def sp(self):
@@ -187,6 +193,28 @@ class _Marshal:
     @property
     def bp(self):
         return self.b.ctypes.data_as(_IP)
+
+
+def _per_seq(x, dtype, batch: int) -> np.ndarray:
+    """One value per sequence, from a scalar or a length-batch sequence."""
+    arr = np.asarray(x, dtype)
+    if arr.ndim == 0:
+        return np.full(batch, arr, dtype)
+    return np.ascontiguousarray(np.broadcast_to(arr, (batch,)))
+
+
+def _size_query(fn: str, *args) -> int:
+    out = ctypes.c_size_t(0)
+    _check(fn, getattr(lib(), fn)(*args, ctypes.byref(out)))
+    return out.value
+
+
+def _ws_args(ws: Optional[torch.Tensor]):
+    """Pointer and byte size of a workspace tensor (the library checks the
+    size against what the call needs and returns WAITS_EWORKSPACE if short)."""
+    if ws is None:
+        return ctypes.c_void_p(0), ctypes.c_size_t(0)
+    return ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size())
 
 
 def _last_dim_contiguous(*ts):
@@ -213,36 +241,26 @@ def first_rows(cu_seqlens, a, b) -> np.ndarray:
 
 def lse_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
     m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
-    out = ctypes.c_size_t(0)
-    _check("waits_lse_workspace_bytes",
-           lib().waits_lse_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
-    return out.value
+    return _size_query("waits_lse_workspace_bytes", m.sp, m.ap, m.bp)
 
 
 def colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
     m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
-    out = ctypes.c_size_t(0)
-    _check("waits_colsum_workspace_bytes",
-           lib().waits_colsum_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
-    return out.value
+    return _size_query("waits_colsum_workspace_bytes", m.sp, m.ap, m.bp)
 
 
 def score_workspace_bytes(q, k, cu_seqlens, a, b, scale=None, pass2: str = "auto") -> int:
     m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
-    out = ctypes.c_size_t(0)
-    _check("waits_score_workspace_bytes",
-           lib().waits_score_workspace_bytes(m.sp, m.ap, m.bp, ctypes.byref(out)))
-    return out.value
+    return _size_query("waits_score_workspace_bytes", m.sp, m.ap, m.bp)
 
 
-def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
-    if nbytes == 0:
+def _workspace(query, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """The caller's workspace as given (the library checks its size), or, if
+    there is none, a new one of the size ``query()`` returns (None if 0)."""
+    if workspace is not None:
         return workspace
-    if workspace is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace needs {nbytes} bytes")
-    return workspace
+    nbytes = query()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
 def lse(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
@@ -253,11 +271,9 @@ def lse(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
     m = _Marshal(cu_seqlens, q, k, scale, a, b)
     if out is None:
         out = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    nbytes = lse_workspace_bytes(q, k, cu_seqlens, a, b, scale)
-    ws = _workspace(nbytes, q.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_lse_workspace_bytes", m.sp, m.ap, m.bp), q.device, workspace)
     _check("waits_lse", lib().waits_lse(
-        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), _ptr(ws),
-        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
+        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), *_ws_args(ws), _stream(q)))
     return out
 
 
@@ -270,11 +286,10 @@ def colsum(q: torch.Tensor, k: torch.Tensor, lse_rows: torch.Tensor, cu_seqlens,
     m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     if out is None:
         out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
-    nbytes = colsum_workspace_bytes(q, k, cu_seqlens, a, b, scale, pass2)
-    ws = _workspace(nbytes, q.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_colsum_workspace_bytes", m.sp, m.ap, m.bp), q.device,
+                    workspace)
     _check("waits_colsum", lib().waits_colsum(
-        m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), _ptr(ws),
-        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
+        m.sp, _ptr(q), _ptr(k), _ptr(lse_rows), m.ap, m.bp, _ptr(out), *_ws_args(ws), _stream(q)))
     return out
 
 
@@ -286,11 +301,10 @@ def score(q: torch.Tensor, k: torch.Tensor, cu_seqlens, a, b, scale=None,
     m = _Marshal(cu_seqlens, q, k, scale, a, b, pass2=pass2)
     if out is None:
         out = torch.empty((k.shape[1], k.shape[0]), dtype=torch.float32, device=k.device)
-    nbytes = score_workspace_bytes(q, k, cu_seqlens, a, b, scale, pass2)
-    ws = _workspace(nbytes, q.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_score_workspace_bytes", m.sp, m.ap, m.bp), q.device,
+                    workspace)
     _check("waits_score", lib().waits_score(
-        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), _ptr(ws),
-        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
+        m.sp, _ptr(q), _ptr(k), m.ap, m.bp, _ptr(out), *_ws_args(ws), _stream(q)))
     return out
 
 
@@ -306,10 +320,7 @@ def _select_shape(cu_seqlens, hkv: int):
 
 def select_workspace_bytes(cu_seqlens, hkv: int, budget: int) -> int:
     shape, _keep = _select_shape(cu_seqlens, hkv)
-    out = ctypes.c_size_t(0)
-    _check("waits_select_workspace_bytes",
-           lib().waits_select_workspace_bytes(ctypes.byref(shape), int(budget), ctypes.byref(out)))
-    return out.value
+    return _size_query("waits_select_workspace_bytes", ctypes.byref(shape), int(budget))
 
 
 def select(scores: torch.Tensor, cu_seqlens, budget: int,
@@ -321,10 +332,10 @@ def select(scores: torch.Tensor, cu_seqlens, budget: int,
     if out is None:
         out = torch.empty((len(cu_c) - 1, hkv, int(budget)), dtype=torch.int32,
                           device=scores.device)
-    ws = _workspace(select_workspace_bytes(cu_c, hkv, budget), scores.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_select_workspace_bytes", ctypes.byref(shape), int(budget)),
+                    scores.device, workspace)
     _check("waits_select", lib().waits_select(
-        ctypes.byref(shape), _ptr(scores), int(budget), _ptr(out), _ptr(ws),
-        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(scores)))
+        ctypes.byref(shape), _ptr(scores), int(budget), _ptr(out), *_ws_args(ws), _stream(scores)))
     return out
 
 
@@ -363,11 +374,11 @@ def select_compact(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_se
         k_out = torch.empty((nb, hkv, int(budget), d), dtype=k.dtype, device=k.device)
     if v_out is None:
         v_out = torch.empty((nb, hkv, int(budget), d), dtype=v.dtype, device=v.device)
-    ws = _workspace(select_workspace_bytes(m.cu, hkv, budget), k.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_select_workspace_bytes", m.sp, int(budget)), k.device,
+                    workspace)
     _check("waits_select_compact", lib().waits_select_compact(
         m.sp, _ptr(scores), _ptr(k), _ptr(v), int(budget), _ptr(idx), _ptr(k_out), _ptr(v_out),
-        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
-        _stream(k)))
+        *_ws_args(ws), _stream(k)))
     return idx, k_out, v_out
 
 
@@ -466,8 +477,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, lens: 
         out = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
-    ws = _workspace(decode_workspace_bytes(q, k_cache, scale), q.device, workspace)
+    ws = _workspace(lambda: _size_query("waits_decode_workspace_bytes", ctypes.byref(sh)), q.device, workspace)
     _check("waits_decode", lib().waits_decode(
         ctypes.byref(sh), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(out), _ptr(lse),
-        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream(q)))
+        *_ws_args(ws), _stream(q)))
     return out, lse
