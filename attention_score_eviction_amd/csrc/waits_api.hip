@@ -477,7 +477,8 @@ FrArgs fr_args(const waits_shape* s, const void* q, const void* k) {
 int run_lse(const waits_shape* s, const void* q, const void* k, const float* a, const int32_t* b,
             float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   const std::vector<Seq> v = plan_seqs(s, a, b, 1);
-  if (ws_bytes < lse_ws_bytes(s, v) || (lse_ws_bytes(s, v) > 0 && !ws)) return WAITS_EWORKSPACE;
+  const size_t need = lse_ws_bytes(s, v);  // (max, sum) float2 partials
+  if (ws_bytes < need || (need > 0 && (!ws || !is_aligned(ws, 8)))) return WAITS_EWORKSPACE;
   const int G = s->n_q_heads / s->n_kv_heads;
   const int hkv = s->n_kv_heads;
   for (int lo = 0; lo < s->batch; lo += MAXB) {

@@ -126,7 +126,10 @@ int waits_lse_workspace_bytes(const waits_shape* shape, const float* a,
  *   lse[g * T + t] = ln sum_{k <= q} exp(scale * <Q[t, g], K[t0 + k, g / G]>)
  * for every processed row q (t = t0 + q, t0 = cu_seqlens[i]).
  * lse: device fp32 [n_q_heads, T], written only at processed rows; other
- * entries are left untouched.  workspace: device, >= waits_lse_workspace_bytes.
+ * entries are left untouched.  workspace: device, 8-byte aligned,
+ * >= waits_lse_workspace_bytes (per-chunk (max, sum) pairs of rows whose keys
+ * are split over several workgroups; WAITS_EWORKSPACE if missing, short or
+ * misaligned).
  */
 int waits_lse(const waits_shape* shape, const void* q, const void* k,
               const float* a, const int32_t* b, float* lse, void* workspace,

@@ -202,6 +202,25 @@ def test_colsum_workspace_validation():
     assert colsum(ctypes.c_void_p(0x100002), need.value) == W.WAITS_EWORKSPACE  # misaligned
 
 
+def test_lse_workspace_validation():
+    # a = 0 at N = 4096 on 32/8 heads: pass 1 splits keys, so it needs room
+    # for its (max, sum) partials, 8-byte aligned
+    s = _shape(n=4096, hq=32, hkv=8)
+    a, b = _ab(a=0.0, b=1)
+    need = ctypes.c_size_t(0)
+    assert W.lib().waits_lse_workspace_bytes(ctypes.byref(s), a.ctypes.data_as(W._FP),
+                                             b.ctypes.data_as(W._IP), ctypes.byref(need)) == 0
+    if need.value == 0:
+        pytest.skip("this plan splits no keys")
+
+    def lse(ws, nbytes):
+        return W.lib().waits_lse(ctypes.byref(s), FAKE, FAKE, a.ctypes.data_as(W._FP),
+                                 b.ctypes.data_as(W._IP), FAKE, ws, nbytes, None)
+    assert lse(None, need.value) == W.WAITS_EWORKSPACE
+    assert lse(FAKE, need.value - 1) == W.WAITS_EWORKSPACE
+    assert lse(ctypes.c_void_p(0x100004), need.value) == W.WAITS_EWORKSPACE  # not 8-byte aligned
+
+
 def test_pass2_plan_validation_and_workspace():
     # the plan field is checked by every call that takes Q
     s = _shape(n=4096, hq=32, hkv=8)
