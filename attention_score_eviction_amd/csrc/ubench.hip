@@ -253,6 +253,136 @@ int run_tile(int threads, int blocks, int iters, float* out, long long* stamps, 
   return 0;
 }
 
+
+// Operand placement in the passes' shape (one cluster at raised priority,
+// four row tiles, the epilogue of the other accumulator set): OP_VGPR lets
+// the compiler keep everything in arch VGPRs; OP_AGPR_AB issues the MFMAs
+// from inline asm with both multiplicands in AGPRs and the accumulators in
+// VGPRs (so only the epilogue's operands go through the VGPR file's read
+// ports); OP_AGPR_ACC holds the accumulators in AGPRs (the epilogue reads
+// them back with v_accvgpr_read).  Timing only: the asm form leaves the
+// compiler no view of the MFMA hazards, so its values are not meaningful.
+enum OperandPlace { OP_VGPR = 0, OP_AGPR_AB = 1, OP_AGPR_ACC = 2 };
+
+template <int TM, int OP>
+__global__ void __launch_bounds__(512) operand_kernel(float* out, long long* stamps, int iters, float c) {
+  constexpr int NT = 4;
+  const int tid = threadIdx.x;
+  bf16x8 a[4], b[2][4];
+  for (int s = 0; s < 4; ++s)
+    for (int i = 0; i < 8; ++i) {
+      a[s][i] = (__bf16)(0.001f * (tid + i + s));
+      b[0][s][i] = (__bf16)(0.002f * (tid - i + s));
+      b[1][s][i] = (__bf16)(0.003f * (tid - i - s));
+    }
+  if constexpr (OP == OP_AGPR_AB) {
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+a"(a[s]));
+  }
+  f32x4 acc[2][2 * NT];
+  for (int p = 0; p < 2; ++p)
+    for (int m = 0; m < 2 * NT; ++m) acc[p][m] = f32x4{0.01f * m, 0.f, 0.f, 0.f};
+  float m4[4] = {0.1f, 0.2f, 0.3f, 0.4f}, sum[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      if constexpr (TM != TM_EPI) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (OP == OP_AGPR_AB) {
+            asm volatile("" : "+a"(b[0][s]));
+            asm volatile("" : "+a"(b[1][s]));
+          } else {
+            asm volatile("" : "+v"(b[0][s]));
+            asm volatile("" : "+v"(b[1][s]));
+          }
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const int m = t * 2 + kt;
+              if constexpr (OP == OP_AGPR_AB) {
+                if (s == 0)
+                  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                               : "=v"(acc[par][m]) : "a"(b[kt][s]), "a"(a[t]));
+                else
+                  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                               : "+v"(acc[par][m]) : "a"(b[kt][s]), "a"(a[t]));
+              } else {
+                acc[par][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    b[kt][s], a[t], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[par][m], 0, 0, 0);
+              }
+            }
+        __builtin_amdgcn_s_setprio(0);
+        if constexpr (OP == OP_AGPR_ACC) {
+#pragma unroll
+          for (int m = 0; m < 2 * NT; ++m) asm volatile("" : "+a"(acc[par][m]));
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2 * NT; ++m) {
+          if constexpr (OP == OP_AGPR_ACC) asm volatile("" : "+a"(acc[par ^ 1][m]));
+          else asm volatile("" : "+v"(acc[par ^ 1][m]));
+        }
+      }
+      if constexpr (TM != TM_MFMA) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float sv = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[par ^ 1][t * 2 + kt][i], c, -m4[t]));
+            sv += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          }
+          sum[t] += sv;
+        }
+      }
+      if constexpr (TM == TM_MIX) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 96, 0);
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  float r = 0.f;
+  for (int p = 0; p < 2; ++p)
+    for (int m = 0; m < 2 * NT; ++m) r += acc[p][m][0] + acc[p][m][3];
+  for (int t = 0; t < 4; ++t) r += sum[t];
+  out[blockIdx.x * blockDim.x + tid] = r;
+  if ((tid & 63) == 0) {
+    const int w = blockIdx.x * (blockDim.x >> 6) + (tid >> 6);
+    stamps[2 * w] = t1 - t0;
+    stamps[2 * w + 1] = r1 - r0;
+  }
+}
+
+template <int TM, int OP>
+int run_operands(int blocks, int iters, float* out, long long* stamps, double* res) {
+  hipLaunchKernelGGL((operand_kernel<TM, OP>), dim3(blocks), dim3(512), 0, 0, out, stamps, 16, 1.0001f);
+  hipLaunchKernelGGL((operand_kernel<TM, OP>), dim3(blocks), dim3(512), 0, 0, out, stamps, iters, 1.0001f);
+  if (hipDeviceSynchronize() != hipSuccess) return 4;
+  const int waves = blocks * 8;
+  std::vector<long long> h((size_t)waves * 2);
+  if (hipMemcpy(h.data(), stamps, sizeof(long long) * h.size(), hipMemcpyDeviceToHost) != hipSuccess) return 4;
+  long long mx = 0, rt = 0;
+  for (int w = 0; w < waves; ++w) {
+    mx = std::max(mx, h[2 * w]);
+    rt = std::max(rt, h[2 * w + 1]);
+  }
+  res[0] = (double)mx / iters;
+  res[1] = (double)mx / ((double)rt / 100e6) / 1e9;
+  return 0;
+}
 }  // namespace
 
 extern "C" {
@@ -429,6 +559,29 @@ int waits_ubench_tile_waves(int blocks, int iters, double* res) {
   rc = rc ? rc : run_tile<TM_MIX, 32, 1, 3, 768>(768, blocks, iters, out, stamps, res + 4);
   rc = rc ? rc : run_tile<TM_MIX, 32, 1, 3, 1024>(1024, blocks, iters, out, stamps, res + 6);
   rc = rc ? rc : run_tile<TM_MIX, 32, 1, 2, 1024>(1024, blocks, iters, out, stamps, res + 8);
+  (void)hipFree(out);
+  (void)hipFree(stamps);
+  return rc;
+}
+
+// Operand placement at two waves per SIMD (512 threads), configurations in
+// order: MFMAs only / MFMAs + epilogue with everything in VGPRs; the same
+// with both multiplicands in AGPRs (inline-asm MFMAs, accumulators in
+// VGPRs); epilogue only / MFMAs + epilogue with the accumulators in AGPRs.
+// res[2 * i + {0, 1}] = cycles per iteration of the slowest wave, clock GHz.
+int waits_ubench_operands(int blocks, int iters, double* res) {
+  if (iters < 2 || iters % 2) return 1;
+  float* out = nullptr;
+  long long* stamps = nullptr;
+  if (hipMalloc(&out, sizeof(float) * blocks * 512) != hipSuccess) return 4;
+  if (hipMalloc(&stamps, sizeof(long long) * 2 * blocks * 8) != hipSuccess) return 4;
+  int rc = 0;
+  rc = rc ? rc : run_operands<TM_MFMA, OP_VGPR>(blocks, iters, out, stamps, res + 0);
+  rc = rc ? rc : run_operands<TM_MIX, OP_VGPR>(blocks, iters, out, stamps, res + 2);
+  rc = rc ? rc : run_operands<TM_MFMA, OP_AGPR_AB>(blocks, iters, out, stamps, res + 4);
+  rc = rc ? rc : run_operands<TM_MIX, OP_AGPR_AB>(blocks, iters, out, stamps, res + 6);
+  rc = rc ? rc : run_operands<TM_EPI, OP_AGPR_ACC>(blocks, iters, out, stamps, res + 8);
+  rc = rc ? rc : run_operands<TM_MIX, OP_AGPR_ACC>(blocks, iters, out, stamps, res + 10);
   (void)hipFree(out);
   (void)hipFree(stamps);
   return rc;

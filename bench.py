@@ -617,6 +617,9 @@ UBENCH_MODES = ["mfma: 8 MFMA 16x16x32 bf16", "triple: 8 (fma, exp, add)", "exp:
                 "split: waves 0-3 8 MFMA, waves 4-7 8 triples",
                 "split: waves 0-3 8 MFMA, waves 4-7 8 fma", "split: waves 0-3 8 MFMA, waves 4-7 8 exp"]
 UBENCH_WAVES = [(512, 4), (768, 4), (768, 3), (1024, 3), (1024, 2)]  # (threads, row tiles per wave)
+UBENCH_OPERANDS = ["MFMAs only, all in VGPRs", "MFMAs + epilogue, all in VGPRs",
+                   "MFMAs only, multiplicands in AGPRs", "MFMAs + epilogue, multiplicands in AGPRs",
+                   "epilogue only, accumulators in AGPRs", "MFMAs + epilogue, accumulators in AGPRs"]
 UBENCH_SELECT = ["start to first barrier (loads issued, LDS cleared)", "pass 1 (top byte, waits for the scores)",
                  "pass 2", "pass 3 (and the L2 requests)", "pass 4", "totals", "output placed", "gather",
                  "total"]
@@ -677,6 +680,16 @@ def ubench(args):
                           "cycles": round(res[2 * i] / (t // 256 * 8 * nt), 2),
                           "clock_ghz": round(res[2 * i + 1], 3)}
                           for i, (t, nt) in enumerate(UBENCH_WAVES)}}), flush=True)
+    # where the MFMA operands and accumulators live (two waves per SIMD)
+    res = (ctypes.c_double * (2 * len(UBENCH_OPERANDS)))()
+    rc = lib.waits_ubench_operands(256, 4000, res)
+    if rc:
+        raise SystemExit(f"waits_ubench_operands failed ({rc})")
+    print(json.dumps({"ubench": "pass shape, one cluster at raised priority, by operand placement "
+                                "(512 threads, 2 waves/SIMD, 4 row tiles)", "workgroups": 256,
+                      "cycles_per_iteration": {m: {"slowest_wave": round(res[2 * i], 1),
+                                                   "clock_ghz": round(res[2 * i + 1], 3)}
+                                               for i, m in enumerate(UBENCH_OPERANDS)}}), flush=True)
 
 
 def main():
