@@ -549,11 +549,9 @@ rowblock_reduce_kernel(const RowBlockReduceArgs args) {
   const int nrb = tab.nrb[p];
   const int64_t R = (int64_t)args.G * max(0, key - tab.q0[p]);
   const int rb0 = (int)min<int64_t>(R / args.rows, nrb - 1);
-  const float* src = args.cpart + tab.ws0[p] + (int64_t)h * N + key;
   const int64_t stride = (int64_t)args.hkv * N;
-  float sum = 0.f;
-  for (int rb = rb0; rb < nrb; ++rb) sum += src[rb * stride];
-  args.scores[(int64_t)h * args.T + tab.tok0[p] + key] = sum;
+  const float* src = args.cpart + tab.ws0[p] + (int64_t)h * N + key + rb0 * stride;
+  args.scores[(int64_t)h * args.T + tab.tok0[p] + key] = ordered_strided_sum(src, stride, nrb - rb0);
 }
 
 }  // namespace waits

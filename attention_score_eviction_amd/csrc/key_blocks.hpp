@@ -288,9 +288,7 @@ colsum_reduce_kernel(const ReduceArgs args) {
   const int key = local - h * N;
   const int64_t at = (int64_t)h * args.T + tab.tok0[p] + key;
   const int64_t stride = (int64_t)args.hkv * args.T;
-  float s = 0.f;
-  for (int rc = 0; rc < tab.nc[p]; ++rc) s += args.part[rc * stride + at];
-  args.scores[at] = s;
+  args.scores[at] = ordered_strided_sum(args.part + at, stride, tab.nc[p]);
 }
 
 }  // namespace waits
