@@ -53,6 +53,7 @@ constexpr int WIDE_SUMS = SEL_THREADS / WIDE_GROUP;    // chunk groups of the cr
 constexpr int WIDE_MAX_CHUNKS = 1024;                  // chunks of the longest accepted head
 constexpr int WIDE_CACHE = 4096;                       // bin-B keys held in LDS
 constexpr int WIDE_FINE_CHUNKS = 64;                   // chunks whose searched offsets stay in LDS
+constexpr int WIDE_U = 4;                              // chunk records per thread loaded together
 // Chunk record: coarse offsets (u32, off[64 j] for j = 0..64), bin offsets
 // (u16, off[b] for b = 0..4096; off[4096] = the chunk's key count), order
 // keys in bin order (u32).  A bin-B key only adds to its chunk's counts, so
@@ -257,12 +258,25 @@ wide_place_kernel(const WideArgs args) {
     const int j = tid & (WIDE_GROUP - 1), g = tid / WIDE_GROUP;
 
     // keys of the head at or above bin 64 j (j < 64)
+    // (WIDE_U chunks per thread with their loads in flight together)
     {
       int s = 0;
-      for (int c = g; c < C; c += WIDE_SUMS) {
-        const int tot = coarse(c, WIDE_GROUPS);
-        s += tot - coarse(c, j);
-        if (j == 0) ctot[c] = tot;
+      for (int c0 = g; c0 < C; c0 += WIDE_U * WIDE_SUMS) {
+        int tot[WIDE_U], at[WIDE_U];
+#pragma unroll
+        for (int u = 0; u < WIDE_U; ++u) {
+          const int c = c0 + u * WIDE_SUMS;
+          tot[u] = c < C ? coarse(c, WIDE_GROUPS) : 0;
+          at[u] = c < C ? coarse(c, j) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < WIDE_U; ++u) {
+          const int c = c0 + u * WIDE_SUMS;
+          if (c < C) {
+            s += tot[u] - at[u];
+            if (j == 0) ctot[c] = tot[u];
+          }
+        }
       }
       red[g][j] = s;
     }
@@ -285,12 +299,24 @@ wide_place_kernel(const WideArgs args) {
     {
       const int b = WIDE_GROUP * gsel + 1 + j;
       int s = 0;
-      for (int c = g; c < C; c += WIDE_SUMS) {
-        const int o = off(c, b);
-        s += ctot[c] - o;
-        if (keep_fine) {
-          fine[c][1 + j] = o;
-          if (j == 0) fine[c][0] = off(c, b - 1);
+      for (int c0 = g; c0 < C; c0 += WIDE_U * WIDE_SUMS) {
+        int o[WIDE_U], o0[WIDE_U];
+#pragma unroll
+        for (int u = 0; u < WIDE_U; ++u) {
+          const int c = c0 + u * WIDE_SUMS;
+          o[u] = c < C ? off(c, b) : 0;
+          o0[u] = keep_fine && j == 0 && c < C ? off(c, b - 1) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < WIDE_U; ++u) {
+          const int c = c0 + u * WIDE_SUMS;
+          if (c < C) {
+            s += ctot[c] - o[u];
+            if (keep_fine) {
+              fine[c][1 + j] = o[u];
+              if (j == 0) fine[c][0] = o0[u];
+            }
+          }
         }
       }
       red[g][j] = s;
