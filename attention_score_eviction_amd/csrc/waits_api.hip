@@ -193,7 +193,7 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
   const int64_t krow = std::max<int64_t>(1, s->kv_stride_tok * elt_bytes(s->dtype));
   const int64_t qrow = std::max<int64_t>(1, s->q_stride_tok * elt_bytes(s->dtype));
   std::vector<Seq> v(s->batch);
-  int64_t fr_units = 0, big_units1 = 0, big_units2 = 0, wide_rg = 0;
+  int64_t fr_units = 0, big_units1 = 0, big_units2 = 0, big_waves = 0, wide_rg = 0;
   for (int i = 0; i < s->batch; ++i) {
     Seq& q = v[i];
     q.n = (int)(s->cu_seqlens[i + 1] - s->cu_seqlens[i]);
@@ -224,12 +224,16 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
       q.nkb = (q.n + KB_KEYS - 1) / KB_KEYS;
       big_units1 += (int64_t)hkv * q.nrb;
       big_units2 += (int64_t)hkv * q.nkb;
+      big_waves += (int64_t)hkv * q.nrb * FR_SHAPES[q.frs].waves;
     }
   }
   for (Seq& q : v) {
     if (q.mode == Mode::FR) {
-      // about 8 waves per compute unit over the batch's few-rows workgroups
-      const int64_t want = std::max<int64_t>(1, ceil_div(8 * NUM_CU, fr_units));
+      // about 8 waves per compute unit over the batch's few-rows workgroups;
+      // in pass 1 the row blocks of the same launch count too, since a key
+      // split there costs the lse combine (pass 2's key chunks need no reduce)
+      const int64_t busy = fr_units + (pass == 1 ? big_waves : 0);
+      const int64_t want = std::max<int64_t>(1, ceil_div(8 * NUM_CU, busy));
       int64_t nc = std::max<int64_t>(1, std::min<int64_t>(want, ceil_div(q.n, FR_MIN_CHUNK)));
       nc = std::max(nc, ceil_div(q.n * krow, SPAN_BYTES));
       q.kc = round32((int)ceil_div(q.n, nc));
