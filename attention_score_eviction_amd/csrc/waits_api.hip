@@ -230,9 +230,10 @@ std::vector<Seq> plan_seqs(const waits_shape* s, const float* a, const int32_t* 
   for (Seq& q : v) {
     if (q.mode == Mode::FR) {
       // about 8 waves per compute unit over the batch's few-rows workgroups;
-      // in pass 1 the row blocks of the same launch count too, since a key
-      // split there costs the lse combine (pass 2's key chunks need no reduce)
-      const int64_t busy = fr_units + (pass == 1 ? big_waves : 0);
+      // in pass 1 of a bf16 batch the row blocks share the launch and count
+      // too, since a key split there costs the lse combine (pass 2's key
+      // chunks need no reduce; fp32 shapes launch one after another)
+      const int64_t busy = fr_units + (pass == 1 && s->dtype == WAITS_BF16 ? big_waves : 0);
       const int64_t want = std::max<int64_t>(1, ceil_div(8 * NUM_CU, busy));
       int64_t nc = std::max<int64_t>(1, std::min<int64_t>(want, ceil_div(q.n, FR_MIN_CHUNK)));
       nc = std::max(nc, ceil_div(q.n * krow, SPAN_BYTES));
