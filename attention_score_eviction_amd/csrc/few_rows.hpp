@@ -28,8 +28,8 @@
 // owns one key and 16 rows per tile; p = exp2(dot * scale*log2 e - off[row])
 // with off = lse * log2 e + log2(1 + exp(-a (q - c))) (w folded in, off =
 // +inf for rows whose fp32 weight is 0).  In-lane sums, then each lane half
-// stores its rows' sum to LDS and the last wave adds the two halves of every
-// wave in a fixed order.  A head in one block has every row here, so that
+// stores its rows' sum to LDS and one wave per sub-tile (8-wave shapes: one
+// per SIMD) adds the two halves of every wave in a fixed order.  A head in one block has every row here, so that
 // sum is the score, written straight to the score array; a head in several
 // blocks writes it as the block's partial (cpart), and rowblock_reduce_kernel
 // adds the blocks in order -- no atomics, bitwise reproducible.
@@ -385,9 +385,15 @@ __device__ __forceinline__ void few_rows_body(const FrArgs& args, const int32_t*
   // pass 2: sub-tile j's per-wave key sums -> its key scores (fixed order)
   // each lane half stores its own rows' sum; the flush adds the two halves
   auto red_store = [&](int j, float csum) { red[j & (2 * FR_SUB - 1)][wave][2 * col + hf] = csum; };
-  // Run by the last wave, which holds no more row tiles than any other.
-  auto flush = [&](int j) {
-    const int ft = tid - (FR_THREADS - WAVE);  // lane of the last wave
+  // Flush slot u of a stage (one sub-tile).  Every wave holds the same row
+  // tiles, so whichever SIMD runs a flush carries it on top of a full share:
+  // with 8 waves, slots 0..3 go to waves 4..7, one per SIMD (waves w and
+  // w + 4 share one), instead of all four to the last wave.  Smaller shapes
+  // flush on their last wave.  Each key's sum keeps the same order.
+  auto flush = [&](int j, int u) {
+    constexpr bool SPREAD = FR_WAVES >= 2 * FR_SUB;
+    const int fw = SPREAD ? FR_WAVES - FR_SUB + u : FR_WAVES - 1;
+    const int ft = tid - fw * WAVE;  // lane of the flushing wave
     if (j >= 0 && j < nsub && ft >= 0 && ft < TILE) {
       const int key = kbeg + j * TILE + ft;
       float sc = 0.f;
@@ -473,7 +479,7 @@ __device__ __forceinline__ void few_rows_body(const FrArgs& args, const int32_t*
       const int buf = (1 + s) & 1;  // == st & 1
       if constexpr (PASS2) {
 #pragma unroll
-        for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - FR_SUB - 1);  // previous stage's epilogues
+        for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - FR_SUB - 1, u);  // previous stage's epilogues
       }
 #pragma unroll
       for (int u = 0; u < FR_SUB; ++u) subtile(buf, u, st * FR_SUB + u);
@@ -489,7 +495,7 @@ __device__ __forceinline__ void few_rows_body(const FrArgs& args, const int32_t*
   if constexpr (PASS2) {
     const int st = nst_pad;  // epilogues of the last stage
 #pragma unroll
-    for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 1);
+    for (int u = 0; u < FR_SUB; ++u) flush(st * FR_SUB + u - 1, u);
   } else {
 #pragma unroll
     for (int t = 0; t < FR_TW; ++t) {
